@@ -1,0 +1,139 @@
+"""fp64 CPU oracle for the Rodimus* token mixer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import this package.  The product path (the HIP library and its binding) never
+does, and shares no code with it.
+
+The arithmetic lives in ``rodimus_oracle.c`` (plain sequential fp64 loops); this
+module compiles it with gcc and wraps it with numpy arrays.  What each function
+computes, and the passages it follows, are stated in the C file's header:
+
+* :func:`gates`  -- the DDTS gate map (our reading; the pages do not print it),
+* :func:`scan`   -- the recurrence S_t = diag(a_t) S_{t-1} + (beta_t*k_t)^T v_t,
+  o_t = q_t S_t, token by token,
+* :func:`decode` -- one step of the same recurrence on a persistent state,
+* :func:`swska`  -- sliding-window attention with one key matrix shared by all
+  heads, dense softmax per query row.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rodimus_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/liboracle.so`` with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp,
+                               _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_gates.argtypes = [dp, dp, ctypes.c_size_t, dp, dp]
+        lib.oracle_gates.restype = None
+        lib.oracle_scan.argtypes = [ctypes.c_int] * 5 + [dp] * 6 + [dp, dp, ctypes.c_int]
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [ctypes.c_int] * 4 + [dp] * 6 + [dp, dp]
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_swska.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 4 +
+                                     [ctypes.POINTER(ctypes.c_longlong), ctypes.c_longlong,
+                                      ctypes.c_int])
+        lib.oracle_swska.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def gates(g, theta):
+    """Return (log a, log beta), elementwise, fp64."""
+    g = _f64(g)
+    theta = _f64(theta)
+    assert g.shape == theta.shape
+    la = np.empty_like(g)
+    lb = np.empty_like(g)
+    _load().oracle_gates(_ptr(g), _ptr(theta), g.size, _ptr(la), _ptr(lb))
+    return la, lb
+
+
+def scan(q, k, v, g, theta, S0=None, nthreads: int = 1):
+    """Sequential recurrence.  q,k,g,theta: [B,H,T,dk]; v: [B,H,T,dv];
+    S0: [B,H,dk,dv] or None.  Returns (o [B,H,T,dv], S_T [B,H,dk,dv]) in fp64."""
+    q, k, v, g, theta = (_f64(x) for x in (q, k, v, g, theta))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for x in (k, g, theta):
+        assert x.shape == q.shape
+    assert v.shape == (B, H, T, dv)
+    if S0 is not None:
+        S0 = _f64(S0)
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv))
+    ST = np.empty((B, H, dk, dv))
+    rc = _load().oracle_scan(B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(theta),
+                             _ptr(S0), _ptr(o), _ptr(ST), int(nthreads))
+    assert rc == 0
+    return o, ST
+
+
+def decode(q, k, v, g, theta, S):
+    """One recurrent step.  q,k,g,theta: [N,H,dk]; v: [N,H,dv]; S: [N,H,dk,dv].
+    Returns (o [N,H,dv], S' [N,H,dk,dv]); the input S is not modified."""
+    q, k, v, g, theta, S = (_f64(x) for x in (q, k, v, g, theta, S))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    assert S.shape == (N, H, dk, dv)
+    o = np.empty((N, H, dv))
+    S_out = np.empty_like(S)
+    rc = _load().oracle_decode(N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(theta),
+                               _ptr(S), _ptr(o), _ptr(S_out))
+    assert rc == 0
+    return o, S_out
+
+
+def swska(q, k_shared, v, window: int, scale=None, rows=None, nthreads: int = 1):
+    """Sliding-window shared-key attention.  q: [B,H,T,dk]; k_shared: [B,T,dk];
+    v: [B,H,T,dv].  ``rows``: optional flat indices (b*H+h)*T+t of the query rows
+    to compute; the others are returned as NaN.  Returns o [B,H,T,dv] fp64."""
+    q, k_shared, v = (_f64(x) for x in (q, k_shared, v))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k_shared.shape == (B, T, dk) and v.shape == (B, H, T, dv)
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    o = np.full((B, H, T, dv), np.nan)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rp = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong))
+        nr = rows.size
+    else:
+        rp, nr = None, 0
+    rc = _load().oracle_swska(B, H, T, dk, dv, int(window), float(scale), _ptr(q), _ptr(k_shared),
+                              _ptr(v), _ptr(o), rp, nr, int(nthreads))
+    assert rc == 0
+    return o
