@@ -1,0 +1,159 @@
+"""Thin Python binding of librodimus.so (the MI355X Rodimus* token-mixer kernels).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/rodimus.h``.  PyTorch supplies
+device memory and the current HIP stream; nothing here computes.
+
+Entry points (same names as the C ABI):
+
+* :func:`rodimus_scan_prefill` -- chunkwise-parallel prefill of the DDTS-gated
+  recurrence; returns ``(o, S_T)``.
+* :func:`rodimus_decode_step`  -- one recurrent step on a resident state
+  (in place by default); returns ``o``.
+* :func:`sw_ska_attn`          -- sliding-window shared-key attention; returns ``o``.
+
+If the shared library has not been built, importing works but every call
+raises ``RuntimeError``; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librodimus.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+F32, BF16 = 0, 1
+EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill", "rodimus_decode_step",
+            "sw_ska_attn", "rodimus_status_string")
+
+_lib = None
+
+
+class RodimusError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m gated_linear_attention_ddts_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.rodimus_scan_prefill_workspace_bytes.argtypes = [i] * 7
+        L.rodimus_scan_prefill_workspace_bytes.restype = sz
+        L.rodimus_scan_prefill.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
+        L.rodimus_scan_prefill.restype = i
+        L.rodimus_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
+        L.rodimus_decode_step.restype = i
+        L.sw_ska_attn.argtypes = [vp] * 4 + [i] * 6 + [ctypes.c_float, i, vp]
+        L.sw_ska_attn.restype = i
+        L.rodimus_status_string.argtypes = [i]
+        L.rodimus_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rodimus_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise RodimusError(status, where)
+
+
+def rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, chunk=64, dtype=BF16) -> int:
+    return int(lib().rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, chunk, dtype))
+
+
+def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S_T=None,
+                         want_state: bool = True, workspace=None,
+                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q, k, g, tau: [B,H,T,dk]; v: [B,H,T,dv]; S0: [B,H,dk,dv] float32 or None.
+    Returns (o [B,H,T,dv], S_T [B,H,dk,dv] float32 or None)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for x in (k, g, tau, v):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau must share one dtype")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, chunk, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rodimus_scan_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S0),
+                                    _ptr(o), _ptr(S_T), B, H, T, dk, dv, chunk, dt,
+                                    _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "rodimus_scan_prefill")
+    return o, S_T
+
+
+def rodimus_decode_step(q, k, v, g, tau, S_in, S_out=None, *, o=None, stream=None) -> torch.Tensor:
+    """q, k, g, tau: [N,H,dk]; v: [N,H,dv]; S_in: [N,H,dk,dv] float32.
+    S_out defaults to S_in (update in place).  Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if S_out is None:
+        S_out = S_in
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib().rodimus_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S_in),
+                                   _ptr(S_out), _ptr(o), N, H, dk, dv, dt, _stream(stream))
+    _check(st, "rodimus_decode_step")
+    return o
+
+
+def sw_ska_attn(q, k_shared, v, window: int, scale: Optional[float] = None, *, o=None,
+                stream=None) -> torch.Tensor:
+    """q: [B,H,T,dk]; k_shared: [B,T,dk]; v: [B,H,T,dv].  Returns o [B,H,T,dv]."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    st = lib().sw_ska_attn(_ptr(q), _ptr(k_shared), _ptr(v), _ptr(o), B, H, T, dk, dv, int(window),
+                           float(scale), dt, _stream(stream))
+    _check(st, "sw_ska_attn")
+    return o

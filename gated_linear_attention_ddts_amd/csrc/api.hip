@@ -1,0 +1,133 @@
+// api.hip -- the C ABI of librodimus: argument validation and dispatch.
+// Every check runs before any HIP call; see include/rodimus.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rodimus.h"
+#include "launch.h"
+
+namespace rodimus {
+
+static bool ok_ptr(const void *p) { return p != nullptr && ((uintptr_t)p & 15) == 0; }
+static bool ok_opt_ptr(const void *p) { return p == nullptr || ((uintptr_t)p & 15) == 0; }
+static bool ok_head_dim(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+static bool ok_dtype(int dt) { return dt == RODIMUS_F32 || dt == RODIMUS_BF16; }
+
+static int hip_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? RODIMUS_OK : RODIMUS_ERR_HIP;
+}
+
+__global__ void state_copy_kernel(const float *__restrict__ src, float *__restrict__ dst, size_t n) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) dst[i] = src ? src[i] : 0.f;
+}
+
+void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st) {
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) return;
+    hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st, S0, S_T, n);
+}
+
+}  // namespace rodimus
+
+using namespace rodimus;
+
+extern "C" {
+
+const char *rodimus_status_string(int status) {
+    switch (status) {
+        case RODIMUS_OK: return "RODIMUS_OK";
+        case RODIMUS_ERR_INVALID_ARG: return "RODIMUS_ERR_INVALID_ARG: invalid argument";
+        case RODIMUS_ERR_UNSUPPORTED: return "RODIMUS_ERR_UNSUPPORTED: shape/dtype not compiled";
+        case RODIMUS_ERR_HIP: return "RODIMUS_ERR_HIP: HIP runtime error";
+        default: return "RODIMUS_UNKNOWN_STATUS";
+    }
+}
+
+static bool scan_sizes_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+    if (B < 0 || H < 0 || T < 0) return false;
+    if (!ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype)) return false;
+    if (!(chunk == 0 || chunk == 16 || chunk == 32 || chunk == 64)) return false;
+    // element counts must fit the kernels' index arithmetic
+    if ((long long)B * H > (1LL << 30)) return false;
+    if ((long long)B * H * T * (dk > dv ? dk : dv) > (1LL << 46)) return false;
+    return true;
+}
+
+size_t rodimus_scan_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                            int dtype) {
+    if (!scan_sizes_ok(B, H, T, dk, dv, chunk, dtype)) return 0;
+    return plan_scan(B, H, T, dk, dv, chunk == 0 ? 64 : chunk, dtype).workspace_bytes;
+}
+
+int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void *g,
+                         const void *tau, const float *S0, void *o, float *S_T,
+                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (!scan_sizes_ok(B, H, T, dk, dv, chunk, dtype)) return RODIMUS_ERR_INVALID_ARG;
+    if (!ok_opt_ptr(S0) || !ok_opt_ptr(S_T) || !ok_opt_ptr(workspace))
+        return RODIMUS_ERR_INVALID_ARG;
+    if (S0 && S_T && S0 == S_T) return RODIMUS_ERR_INVALID_ARG;
+    if (chunk == 0) chunk = 64;
+    hipStream_t st = (hipStream_t)stream;
+    if (B == 0 || H == 0) return RODIMUS_OK;
+    const size_t nstate = (size_t)B * H * dk * dv;
+    if (T == 0) {
+        if (S_T) {
+            launch_state_copy(S0, S_T, nstate, st);
+            return hip_status();
+        }
+        return RODIMUS_OK;
+    }
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(o))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanPlan plan = plan_scan(B, H, T, dk, dv, chunk, dtype);
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanArgs a{q, k, v, g, tau, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, workspace,
+               workspace_bytes};
+    if (plan.mfma) launch_scan_mfma(a, plan, st);
+    else launch_scan_generic(a, st);
+    return hip_status();
+}
+
+int rodimus_decode_step(const void *q, const void *k, const void *v, const void *g,
+                        const void *tau, const float *S_in, float *S_out, void *o,
+                        int N, int H, int dk, int dv, int dtype, void *stream) {
+    if (N < 0 || H < 0 || !ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype))
+        return RODIMUS_ERR_INVALID_ARG;
+    if ((long long)N * H > (1LL << 30)) return RODIMUS_ERR_INVALID_ARG;
+    if (N == 0 || H == 0) return RODIMUS_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(S_in) ||
+        !ok_ptr(S_out) || !ok_ptr(o))
+        return RODIMUS_ERR_INVALID_ARG;
+    // S_out must equal S_in or not overlap it at all.
+    const size_t sbytes = (size_t)N * H * dk * dv * sizeof(float);
+    const char *a0 = (const char *)S_in, *b0 = (const char *)S_out;
+    if (a0 != b0 && a0 < b0 + sbytes && b0 < a0 + sbytes) return RODIMUS_ERR_INVALID_ARG;
+    DecodeArgs a{q, k, v, g, tau, S_in, S_out, o, N, H, dk, dv, dtype};
+    launch_decode_step(a, (hipStream_t)stream);
+    return hip_status();
+}
+
+int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
+                int B, int H, int T, int dk, int dv, int window, float scale, int dtype,
+                void *stream) {
+    if (B < 0 || H < 0 || T < 0 || window < 1 || !ok_head_dim(dk) || !ok_head_dim(dv) ||
+        !ok_dtype(dtype))
+        return RODIMUS_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !(scale < 3.0e38f)) return RODIMUS_ERR_INVALID_ARG;
+    if ((long long)B * H * T * (dk > dv ? dk : dv) > (1LL << 46)) return RODIMUS_ERR_INVALID_ARG;
+    if (!swska_supported(dk, dv, dtype)) return RODIMUS_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) return RODIMUS_OK;
+    if (!ok_ptr(q) || !ok_ptr(k_shared) || !ok_ptr(v) || !ok_ptr(o)) return RODIMUS_ERR_INVALID_ARG;
+    SkaArgs a{q, k_shared, v, o, B, H, T, dk, dv, window, scale, dtype};
+    launch_swska(a, (hipStream_t)stream);
+    return hip_status();
+}
+
+}  // extern "C"

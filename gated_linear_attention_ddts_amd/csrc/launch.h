@@ -1,0 +1,49 @@
+// launch.h -- host-side launchers behind the C ABI (validated arguments only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace rodimus {
+
+struct ScanArgs {
+    const void *q, *k, *v, *g, *tau;
+    const float *S0;  // nullable
+    void *o;
+    float *S_T;       // nullable
+    int B, H, T, dk, dv, chunk, dtype;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *tau;
+    const float *S_in;
+    float *S_out;
+    void *o;
+    int N, H, dk, dv, dtype;
+};
+
+struct SkaArgs {
+    const void *q, *k, *v;
+    void *o;
+    int B, H, T, dk, dv, window;
+    float scale;
+    int dtype;
+};
+
+// Segment plan of the prefill: number of T-segments per (b,h) and workspace.
+struct ScanPlan {
+    bool mfma;     // bf16, dk = dv = 128 MFMA kernel
+    int segments;  // >= 1
+    size_t workspace_bytes;
+};
+ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+void launch_decode_step(const DecodeArgs &a, hipStream_t st);
+void launch_scan_generic(const ScanArgs &a, hipStream_t st);
+void launch_scan_mfma(const ScanArgs &a, const ScanPlan &p, hipStream_t st);
+void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st);
+bool swska_supported(int dk, int dv, int dtype);
+void launch_swska(const SkaArgs &a, hipStream_t st);
+
+}  // namespace rodimus

@@ -1,0 +1,145 @@
+/*
+ * rodimus.h -- C ABI of the MI355X (gfx950) Rodimus* token-mixer library
+ *              (librodimus.so).
+ *
+ * The library computes three operations of the Rodimus* token mixer, each in
+ * hand-written HIP kernels launched asynchronously on the caller's stream:
+ *
+ *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
+ *                        whole prompt, in chunkwise-parallel form;
+ *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
+ *  sw_ska_attn           sliding-window attention with one key matrix shared
+ *                        by all heads (SW-SKA).
+ *
+ * Sources.  The Rodimus block paragraph of "ICLR 2025 | Rodimus*: ..."
+ * (CodeFuse article) describes the recurrent state with a selection gate, a
+ * temperature gate and an input gate, trained chunkwise in parallel with
+ * sub-quadratic cost and run at inference with an O(1)-size state; the page
+ * does not print the formula.  This library computes, per (batch b, head h),
+ * with S in R^{dk x dv} (rows = key channels):
+ *
+ *     log a_t    = -sigmoid(tau_t) * softplus(-g_t)          (per key channel)
+ *     log beta_t = -sigmoid(tau_t) * softplus( g_t)
+ *     S_t = diag(a_t) S_{t-1} + (beta_t * k_t)^T v_t,        o_t = q_t S_t
+ *
+ * i.e. a = s^T, beta = (1 - s)^T with selection s = sigmoid(g) and temperature
+ * T = sigmoid(tau); tau = 0 gives the tempered_gate_init of 0.5 listed in the
+ * module configuration (section 3 of the Rodimus* deployment blog,
+ * m.nxbn.cn/news/205411).  SW-SKA follows the SKA / Rodimus+ paragraphs and
+ * Fig. 4 of the CodeFuse article (keys shared across heads, values per head),
+ * with softmax(q k^T * scale) v (MiniCPM-SALA blog, wzjinhao.cn/news/68323,
+ * section 1.1) restricted to the previous `window` keys including the query's
+ * own position (same blog, section 2.1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers are DEVICE pointers (hipMalloc'd or equivalent) owned by the
+ *    caller; the library keeps no pointer after the call returns, allocates
+ *    nothing and has no mutable global state (thread-safe).
+ *  - Tensors are contiguous, row-major, 16-byte aligned.
+ *  - dtype selects the element type of q, k, v, g, tau and o:
+ *    RODIMUS_F32 (float) or RODIMUS_BF16 (bfloat16 bit patterns).  Recurrent
+ *    states are always float.  Internal arithmetic is fp32 (MFMA operands
+ *    bf16 with fp32 accumulation on the bf16 path); o is rounded to nearest
+ *    even.
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work; nothing is synchronised inside the library.
+ *  - Arguments are validated before any HIP call.  On a non-OK return nothing
+ *    has been launched, except RODIMUS_ERR_HIP (a launch error reported by the
+ *    runtime).  No exception crosses the ABI.
+ *  - Inputs must be finite, except tau = -inf, which is defined (a = beta = 1).
+ */
+#ifndef RODIMUS_H
+#define RODIMUS_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RODIMUS_OK = 0,
+    RODIMUS_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, small workspace */
+    RODIMUS_ERR_UNSUPPORTED = -2, /* valid but outside the compiled kernel set */
+    RODIMUS_ERR_HIP = -3          /* the HIP runtime reported an error */
+} rodimus_status;
+
+typedef enum { RODIMUS_F32 = 0, RODIMUS_BF16 = 1 } rodimus_dtype;
+
+/*
+ * Bytes of device workspace rodimus_scan_prefill needs for these arguments
+ * (0 when it needs none).  The segment-parallel path used when B*H is too
+ * small to fill the GPU keeps, per segment boundary and (b,h), a float state
+ * [dk x dv] and a float log-decay vector [dk].  Returns 0 for arguments that
+ * rodimus_scan_prefill would reject.
+ */
+size_t rodimus_scan_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                            int dtype);
+
+/*
+ * Chunkwise-parallel prefill of the recurrence above (CodeFuse article,
+ * Rodimus block paragraph: chunkwise-parallel training/prefill form).
+ *
+ *   q, k, g, tau : [B, H, T, dk]      v, o : [B, H, T, dv]     (dtype)
+ *   S0           : [B, H, dk, dv] float, the state before token 0;
+ *                  NULL means zeros.
+ *   S_T          : [B, H, dk, dv] float, receives the state after token T-1;
+ *                  NULL skips it.  May not alias S0.
+ *   chunk        : C in {16, 32, 64}, or 0 for 64.  The result does not depend
+ *                  on C beyond rounding.
+ *   workspace    : device scratch of at least
+ *                  rodimus_scan_prefill_workspace_bytes(...) bytes (may be
+ *                  NULL when that is 0).  Its contents are overwritten.
+ *
+ * Sizes: B, H, T >= 0 (T = 0 copies S0, or zeros, to S_T); dk, dv multiples
+ * of 16 in [16, 128].  A too-small workspace gives RODIMUS_ERR_INVALID_ARG.
+ */
+int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void *g,
+                         const void *tau, const float *S0, void *o, float *S_T,
+                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent (decode) step for N independent sequences (CodeFuse article,
+ * Rodimus block paragraph: O(1)-size state at inference; the state stays
+ * resident and is updated in place, MiniCPM-SALA blog section 3.3):
+ *
+ *   S' = diag(a) S + (beta * k)^T v,   o = q S'
+ *
+ *   q, k, g, tau : [N, H, dk]   v, o : [N, H, dv]   (dtype)
+ *   S_in, S_out  : [N, H, dk, dv] float; S_out may equal S_in (in place) but
+ *                  must not partially overlap it.
+ *
+ * Sizes: N, H >= 0; dk, dv multiples of 16 in [16, 128].
+ */
+int rodimus_decode_step(const void *q, const void *k, const void *v, const void *g,
+                        const void *tau, const float *S_in, float *S_out, void *o,
+                        int N, int H, int dk, int dv, int dtype, void *stream);
+
+/*
+ * Sliding-window shared-key attention (CodeFuse article, SKA and Rodimus+
+ * paragraphs, Fig. 4; window semantics from the MiniCPM-SALA blog, sections
+ * 1.1 and 2.1):
+ *
+ *   o[b,h,t] = sum_{s=max(0,t-window+1)}^{t} softmax_s(scale * q[b,h,t].k[b,s]) v[b,h,s]
+ *
+ *   q : [B, H, T, dk]   k_shared : [B, T, dk]   v, o : [B, H, T, dv]
+ *   scale : usually 1/sqrt(dk); must be finite and > 0.
+ *   window >= 1 (window >= T is causal attention over the whole prefix).
+ *
+ * No rotary embedding is applied: pass rotated q and k.  Supported:
+ * RODIMUS_BF16 with dk = dv = 128 or dk = dv = 64; other combinations return
+ * RODIMUS_ERR_UNSUPPORTED.  B, H, T >= 0.
+ */
+int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
+                int B, int H, int T, int dk, int dv, int window, float scale, int dtype,
+                void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *rodimus_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RODIMUS_H */

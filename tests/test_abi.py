@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_attention_ddts_amd as rd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rodimus.h")
+
+FAKE = 0x10000          # aligned, non-null; never dereferenced (validation fails first)
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_five_entry_points():
+    assert declared_functions() == sorted(rd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(rd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in (rd.OK, rd.ERR_INVALID_ARG, rd.ERR_UNSUPPORTED, rd.ERR_HIP):
+        s = rd.status_string(code)
+        assert s.startswith("RODIMUS_")
+    assert rd.status_string(12345) == "RODIMUS_UNKNOWN_STATUS"
+
+
+def scan(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S0=None, o=FAKE, S_T=None, B=1, H=1, T=8,
+             dk=16, dv=16, chunk=64, dtype=rd.BF16, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_prefill(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S0"], a["o"],
+                                         a["S_T"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                         a["chunk"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(tau=None), dict(o=None),
+    dict(q=MISALIGNED), dict(S0=MISALIGNED), dict(S_T=MISALIGNED),
+    dict(B=-1), dict(H=-2), dict(T=-1), dict(dk=8), dict(dk=24), dict(dk=144), dict(dv=0),
+    dict(dv=136), dict(chunk=8), dict(chunk=128), dict(chunk=-64), dict(dtype=2), dict(dtype=-1),
+    dict(S0=FAKE, S_T=FAKE),
+])
+def test_scan_rejects(kw):
+    assert scan(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_scan_empty_batch_is_noop():
+    assert scan(B=0, q=None, k=None) == rd.OK
+    assert scan(H=0, o=None) == rd.OK
+    # T == 0 without S_T launches nothing
+    assert scan(T=0, q=None, o=None) == rd.OK
+
+
+def test_workspace_query():
+    assert rd.rodimus_scan_prefill_workspace_bytes(1, 1, 8, 8, 16, 64, rd.BF16) == 0  # invalid dk
+    n = rd.rodimus_scan_prefill_workspace_bytes(1, 16, 131072, 128, 128, 64, rd.BF16)
+    assert n >= 0
+    assert rd.rodimus_scan_prefill_workspace_bytes(4, 16, 4096, 128, 128, 0, rd.BF16) >= 0
+
+
+def decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S_in=FAKE, S_out=FAKE, o=FAKE, N=2, H=2,
+             dk=16, dv=16, dtype=rd.BF16, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_decode_step(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S_in"],
+                                        a["S_out"], a["o"], a["N"], a["H"], a["dk"], a["dv"],
+                                        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(S_in=None), dict(S_out=None), dict(o=None), dict(v=MISALIGNED),
+    dict(N=-1), dict(H=-1), dict(dk=0), dict(dv=20), dict(dtype=7),
+    dict(S_out=FAKE + 16),  # partial overlap with S_in
+])
+def test_decode_rejects(kw):
+    assert decode(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_decode_empty_is_noop():
+    assert decode(N=0, q=None) == rd.OK
+
+
+def ska(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=2, T=16, dk=128, dv=128, window=4,
+             scale=0.088, dtype=rd.BF16, stream=None)
+    a.update(kw)
+    return rd.lib().sw_ska_attn(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["T"], a["dk"],
+                                a["dv"], a["window"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(window=0), dict(window=-3), dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")),
+    dict(scale=float("nan")), dict(B=-1), dict(T=-5), dict(dk=7), dict(dtype=3),
+])
+def test_swska_rejects(kw):
+    assert ska(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_swska_unsupported_shapes():
+    assert ska(dk=128, dv=64) == rd.ERR_UNSUPPORTED
+    assert ska(dk=32, dv=32) == rd.ERR_UNSUPPORTED
+    assert ska(dtype=rd.F32) == rd.ERR_UNSUPPORTED
