@@ -1,0 +1,252 @@
+"""Benchmark of the Rodimus* token-mixer hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-extras]
+
+A step is one rodimus_scan_prefill call over the 1.6B-shaped prefill batch
+(B=4, T=4096, H=16, dk=dv=128, bf16 inputs, fp32 state, C=64) with every input
+already resident in HBM.  value = B*T / step time (prefill tokens/s).  The
+decode state update (256 sequences x 16 heads, fp32 128x128 states, 1000
+in-place steps cycling over 8 resident input sets) is timed in the same run and
+reported as HBM GB/s and fraction of peak, as the metric asks.  The long-context
+prefill (T=131072) and SW-SKA (T=32768, w=4096) are timed as extras.
+
+Timing: W untimed warm-up steps, then K steps between two HIP events on the
+stream the kernels run on (torch's current stream), with device syncs on both
+sides.  Algorithmic bytes per token-head of the prefill: q, k, g, tau (4 x 256 B)
++ v (256 B) in, o (256 B) out = 1536 B, plus the fp32 final state.  Decode:
+the fp32 state read and written (2 x 64 KiB per head) plus 5 x 256 B inputs and
+256 B output per head.  Peaks: HBM 8 TB/s; dense bf16 MFMA 2.5 PFLOP/s.
+
+The CPU baseline is the fp64 oracle run on the host cores over a bounded sample
+of the same workload (stated in the "sample" field).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (H16,d128,T4K) + decode state-update HBM GB/s, % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+NAMES = ("q", "k", "v", "g", "theta")
+
+
+def _dev(t):
+    import torch
+    if t.dtype == "fp32":
+        return torch.from_numpy(np.ascontiguousarray(t.values)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.storage().view(np.int16))).cuda().view(torch.bfloat16)
+
+
+def _time(fn, steps, warmup):
+    """Average GPU time (ms) of fn() over `steps` calls, HIP events on torch's stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def prefill_bytes(B, H, T, dk, dv):
+    return B * H * T * (4 * dk * 2 + dv * 2 + dv * 2) + B * H * dk * dv * 4
+
+
+def prefill_flops(B, H, T, dk, dv, C):
+    # causal-triangle count: 4 dk dv (state in/out) + (C+1)(dk+dv) intra-chunk per token-head
+    return B * H * T * (4 * dk * dv + (C + 1) * (dk + dv))
+
+
+def bench_prefill(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    x = workloads.scan_inputs(cfg["seed"], cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"],
+                              cfg["dtype"], gate_mu=cfg["gate_mu"])
+    d = {n: _dev(x[n]) for n in NAMES}
+    del x
+    B, H, T, dk, dv, C = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"], cfg["chunk"]
+    o = torch.empty(B, H, T, dv, dtype=d["q"].dtype, device="cuda")
+    ST = torch.empty(B, H, dk, dv, dtype=torch.float32, device="cuda")
+    nws = rd.rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, C, rd.BF16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rd.rodimus_scan_prefill(d["q"], d["k"], d["v"], d["g"], d["theta"], None, C, o=o, S_T=ST,
+                                workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    nbytes = prefill_bytes(B, H, T, dk, dv)
+    flops = prefill_flops(B, H, T, dk, dv, C)
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
+                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+                workspace_bytes=nws)
+
+
+def bench_decode(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    N, H, dk, dv = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"]
+    sets = workloads.decode_pool(cfg["seed"], N, H, dk, dv, pool=cfg["pool"], dtype=cfg["dtype"])
+    dsets = [{n: _dev(s[n]) for n in NAMES} for s in sets]
+    S = torch.zeros(N, H, dk, dv, dtype=torch.float32, device="cuda")
+    o = torch.empty(N, H, dv, dtype=torch.bfloat16, device="cuda")
+    state = {"s": 0}
+
+    def step():
+        s = dsets[state["s"] % len(dsets)]
+        state["s"] += 1
+        rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], S, o=o)
+
+    ms = _time(step, steps, warmup)
+    nbytes = N * H * (2 * dk * dv * 4 + (3 * dk + dv + dk) * 2 + dv * 2)
+    return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+
+
+def bench_swska(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    B, H, T, dk, dv, w = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"], cfg["window"]
+    x = workloads.swska_inputs(cfg["seed"], B, H, T, dk, dv)
+    d = {n: _dev(x[n]) for n in ("q", "k", "v")}
+    o = torch.empty(B, H, T, dv, dtype=torch.bfloat16, device="cuda")
+    try:
+        rd.sw_ska_attn(d["q"], d["k"], d["v"], w, o=o)
+    except rd.RodimusError as ex:
+        return dict(status=str(ex))
+
+    def step():
+        rd.sw_ska_attn(d["q"], d["k"], d["v"], w, o=o)
+
+    ms = _time(step, steps, warmup)
+    # query-key pairs inside the window (causal band), 4*d flops each
+    pairs = 0
+    for t in range(T):
+        pairs += min(t + 1, w)
+    pairs *= B * H
+    flops = pairs * 2 * (dk + dv)
+    nbytes = (B * H * T * (dk + 2 * dv) + B * T * dk) * 2
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), flops=flops,
+                tflops=flops / (ms * 1e-3) / 1e12, bytes=nbytes)
+
+
+def cpu_baseline(cfg):
+    """The fp64 oracle on the host cores over a bounded sample of the prefill
+    workload: the first `heads` (b, h) pairs, full sequence length."""
+    import oracle
+    import workloads
+    cores = min(os.cpu_count() or 1, 16)
+    heads = min(cfg["B"] * cfg["H"], max(cores, 16))
+    x = workloads.scan_inputs(cfg["seed"], cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"],
+                              cfg["dtype"], gate_mu=cfg["gate_mu"])
+    BH = cfg["B"] * cfg["H"]
+    flat = {n: x[n].values.reshape(1, BH, cfg["T"], -1)[:, :heads].astype(np.float64) for n in NAMES}
+    t0 = time.perf_counter()
+    oracle.scan(*(flat[n] for n in NAMES), nthreads=cores)
+    dt = time.perf_counter() - t0
+    # tokens/s of the whole B x T batch at this rate (every (b,h) costs the same)
+    token_heads_per_s = heads * cfg["T"] / dt
+    return dict(value=token_heads_per_s / cfg["H"], unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{heads} of {BH} (b,h) pairs x T={cfg['T']} (fp64 sequential scan, "
+                       f"{dt:.2f} s); rate scaled to B*T tokens over H={cfg['H']} heads")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (b,h) pair and segment is independent per GPU; see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    cfg = workloads.CONFIGS["prefill_1p6b_T4096"]
+    print("bench: prefill_1p6b_T4096", file=sys.stderr, flush=True)
+    pre = bench_prefill(cfg, args.steps, args.warmup)
+    print("bench: decode_N256", file=sys.stderr, flush=True)
+    dec = bench_decode(workloads.CONFIGS["decode_N256"], args.decode_steps, 10)
+
+    extras = {}
+    if not args.no_extras:
+        print("bench: prefill_long_T131072", file=sys.stderr, flush=True)
+        lc = workloads.CONFIGS["prefill_long_T131072"]
+        r = bench_prefill(lc, max(3, args.steps // 4), 1)
+        extras["prefill_long_T131072"] = dict(
+            ms=round(r["ms"], 4), tokens_per_s=round(r["tokens_per_s"]),
+            gbs=round(r["gbs"], 1), frac_hbm=round(r["gbs"] / HBM_PEAK_GBS, 4),
+            mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
+        print("bench: swska_T32768_w4096", file=sys.stderr, flush=True)
+        sc = workloads.CONFIGS["swska_T32768_w4096"]
+        r = bench_swska(sc, max(3, args.steps // 4), 1)
+        if "ms" in r:
+            r = dict(ms=round(r["ms"], 4), tokens_per_s=round(r["tokens_per_s"]),
+                     tflops=round(r["tflops"], 1),
+                     frac_mfma=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
+        extras["swska_T32768_w4096"] = r
+
+    cpu = None
+    if not args.no_cpu:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg)
+        cpu["value"] = round(cpu["value"], 1)
+
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_1p6b_T4096", "B": cfg["B"], "T": cfg["T"], "H": cfg["H"],
+                   "dk": cfg["dk"], "dv": cfg["dv"], "chunk": cfg["chunk"],
+                   "state_dtype": "fp32"},
+        "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "rodimus_scan_prefill (one call)",
+                     "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "decode": {"workload": "decode_N256", "us_per_step": round(dec["us_per_step"], 2),
+                   "tokens_per_s": round(dec["tokens_per_s"]), "gbs": round(dec["gbs"], 1),
+                   "frac_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4), "steps": dec["steps"]},
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,6 +69,19 @@ __device__ __forceinline__ void ddts_log2_gates(float g, float theta, float &l2a
     l2b = -tau * (fmaxf(g, 0.f) * kLog2e + L2);
 }
 
+// Cheaper base-2 gate map for the bf16 MFMA path (no division, no select):
+//   tau = 1 / (1 + 2^{-theta log2 e})   (theta = -inf -> 1/inf = 0, +inf -> 1)
+//   L2  = log2(1 + 2^{-|g| log2 e})     (absolute error ~2^-24; relative error of
+//                                         small L2 grows as |g| grows, which stays
+//                                         far below the bf16 operand rounding)
+//   log2 a = -tau (max(-g,0) log2 e + L2),   log2 beta = -tau (max(g,0) log2 e + L2)
+__device__ __forceinline__ void ddts_log2_gates_fast(float g, float theta, float &l2a, float &l2b) {
+    const float tau = __builtin_amdgcn_rcpf(1.f + exp2_fast(-theta * kLog2e));
+    const float L2 = log2_fast(1.f + exp2_fast(-fabsf(g) * kLog2e));
+    l2a = -tau * fmaf(fmaxf(-g, 0.f), kLog2e, L2);
+    l2b = -tau * fmaf(fmaxf(g, 0.f), kLog2e, L2);
+}
+
 __device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace rodimus

@@ -1,10 +1,284 @@
-// swska.hip -- placeholder: the SW-SKA kernel is not built yet.
+// swska.hip -- sliding-window shared-key attention (SW-SKA) on gfx950.
+//
+//   o[b,h,t] = sum_{s = max(0, t-w+1)}^{t} softmax_s(scale * q[b,h,t] . k[b,s]) v[b,h,s]
+//
+// One key matrix is shared by all heads while every head keeps its own values
+// (SKA, "ICLR 2025 | Rodimus*: ..." (CodeFuse), SKA / Rodimus+ paragraphs and
+// Fig. 4), inside sliding-window attention where each query sees the previous
+// w keys including itself (MiniCPM-SALA blog, sections 1.1 and 2.1).
+//
+// Kernel: one workgroup = 128 consecutive queries of one (b, h); 4 waves, 32
+// queries each.  Keys/values stream through LDS in tiles of 64 (double
+// buffered; the next tile is fetched into registers while the current one is
+// used).  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+//   S^T = K Q^T       keys on the M dimension, queries on lanes, so each lane
+//                     owns one query's scores and the softmax reductions stay
+//                     inside the lane (plus one exchange with lane^32);
+//   online softmax    fp32, base 2, scale folded into one FMA; the output is
+//                     rescaled only when a lane's running max grows by more than
+//                     2^8 (exact: the final division uses the same reference);
+//   O^T += V^T P^T    P^T taken straight from the S^T accumulators (bf16) with a
+//                     permuted k order; V^T is read from LDS with the same order.
+// Tiles entirely outside a wave's window are skipped; tiles on the window's two
+// edges are masked element by element.  Workgroups are mapped so that each XCD
+// works on a fixed pair of heads in increasing query order, which keeps the
+// shared K and the per-head V of overlapping windows in that XCD's L2.
 #include "device_common.h"
 #include "launch.h"
 
 namespace rodimus {
 
-bool swska_supported(int dk, int dv, int dtype) { (void)dk; (void)dv; (void)dtype; return false; }
-void launch_swska(const SkaArgs &a, hipStream_t st) { (void)a; (void)st; }
+namespace {
+
+constexpr int kBQ = 128;
+constexpr int kBK = 64;
+constexpr float kRescale = 8.f;  // log2 of the largest p before the output is rescaled
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Tile {
+    static constexpr int KROW = D + 8;        // bf16 per K row in LDS
+    static constexpr int VROW = kBK + 8;      // bf16 per V^T row in LDS
+    static constexpr int KBYTES = kBK * KROW * 2;
+    static constexpr int VBYTES = D * VROW * 2;
+    static constexpr int BYTES = KBYTES + VBYTES;
+    static constexpr int KVEC = kBK * D / 8 / 256;  // 16-byte K vectors per thread
+    static constexpr int KPT = D / 32;              // keys per thread in the V transpose
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_tile(const bf16_t *__restrict__ kb, const bf16_t *__restrict__ vb,
+                                           int k0, int T, uint4 (&rk)[Tile<D>::KVEC],
+                                           uint4 (&rv)[Tile<D>::KPT]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < Tile<D>::KVEC; ++i) {
+        const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
+        const int key = k0 + row;
+        rk[i] = key < T ? *reinterpret_cast<const uint4 *>(kb + (size_t)key * D + 8 * col)
+                        : make_uint4(0, 0, 0, 0);
+    }
+    constexpr int KPT = Tile<D>::KPT;
+    const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int key = k0 + KPT * kg + i;
+        rv[i] = key < T ? *reinterpret_cast<const uint4 *>(vb + (size_t)key * D + 8 * dg)
+                        : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D>::KVEC],
+                                           const uint4 (&rv)[Tile<D>::KPT]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < Tile<D>::KVEC; ++i) {
+        const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
+        *reinterpret_cast<uint4 *>(buf + (row * Tile<D>::KROW + 8 * col) * 2) = rk[i];
+    }
+    // V^T: row = value channel, KPT consecutive keys per write
+    constexpr int KPT = Tile<D>::KPT;
+    const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
+    char *vt = buf + Tile<D>::KBYTES;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t w[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const uint32_t word = (e < 2) ? rv[i].x : (e < 4) ? rv[i].y : (e < 6) ? rv[i].z : rv[i].w;
+            w[i] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        }
+        const int off = ((8 * dg + e) * Tile<D>::VROW + KPT * kg) * 2;
+        if (KPT == 4) {
+            *reinterpret_cast<uint2 *>(vt + off) =
+                make_uint2(w[0] | (w[1 % KPT] << 16), w[2 % KPT] | (w[3 % KPT] << 16));
+        } else {
+            *reinterpret_cast<uint32_t *>(vt + off) = w[0] | (w[1 % KPT] << 16);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2)
+void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+                  const bf16_t *__restrict__ v, bf16_t *__restrict__ o,
+                  int BH, int H, int T, int window, float scale_log2e, int nqb) {
+    using TL = Tile<D>;
+    __shared__ __attribute__((aligned(16))) char smem[2 * TL::BYTES];
+
+    // XCD-aware block -> (b*H + h, query block): XCD x = id % 8 walks the heads
+    // x, x + 8, ... in increasing query-block order.
+    const int id = blockIdx.x;
+    int bh, qb;
+    if (BH % 8 == 0) {
+        const int xcd = id % 8, slot = id / 8, per = BH / 8;
+        bh = xcd + 8 * (slot % per);
+        qb = slot / per;
+    } else {
+        bh = id % BH;
+        qb = id / BH;
+    }
+    if (qb >= nqb) return;
+    const int b = bh / H;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+    const int q0 = qb * kBQ;
+    const int qw0 = q0 + 32 * w;            // this wave's first query
+    const int qi = qw0 + l32;               // this lane's query
+    const bf16_t *kb = k + (size_t)b * T * D;
+    const bf16_t *vb = v + (size_t)bh * T * D;
+
+    // Q^T operand fragments (B operand: n = query, k = channel)
+    bf16x8_t qB[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        uint4 x = qi < T ? *reinterpret_cast<const uint4 *>(q + ((size_t)bh * T + qi) * D + 16 * s + 8 * h)
+                         : make_uint4(0, 0, 0, 0);
+        qB[s] = __builtin_bit_cast(bf16x8_t, x);
+    }
+
+    f32x16_t O[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) O[mt] = f32x16_t{};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int lo = max(0, q0 - window + 1);
+    const int hi = min(T, q0 + kBQ);        // exclusive
+    const int kt0 = (lo / kBK) * kBK;
+    // this wave's key range [wlo, whi]
+    const int wlo = qw0 - window + 1, whi = qw0 + 31;
+
+    uint4 rk[TL::KVEC], rv[TL::KPT];
+    fetch_tile<D>(kb, vb, kt0, T, rk, rv);
+    store_tile<D>(smem, rk, rv);
+    __syncthreads();
+
+    int buf = 0;
+    for (int k0 = kt0; k0 < hi; k0 += kBK, buf ^= 1) {
+        const bool more = k0 + kBK < hi;
+        if (more) fetch_tile<D>(kb, vb, k0 + kBK, T, rk, rv);
+        const char *cur = smem + buf * TL::BYTES;
+
+        const bool skip = (k0 + kBK - 1 < wlo) || (k0 > whi);
+        if (!skip) {
+            const bool edge = (k0 <= whi - window) || (k0 + kBK - 1 > qw0) || (k0 + kBK > T);
+            // S^T tile: 64 keys x 32 queries
+            f32x16_t S[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                S[mt] = f32x16_t{};
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                        cur + ((32 * mt + l32) * TL::KROW + 16 * s + 8 * h) * 2);
+                    S[mt] = mfma(a, qB[s], S[mt]);
+                }
+            }
+            if (edge) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+                        const bool ok = key <= qi && key > qi - window && key < T;
+                        S[mt][i] = ok ? S[mt][i] : -INFINITY;
+                    }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mt][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = mx * scale_log2e;   // scale > 0 keeps the order
+            const bool grow = mnew > m + kRescale;
+            if (__any(grow)) {
+                const float corr = grow ? exp2_fast(m - mnew) : 1.f;  // m = -inf -> 0
+                if (grow) m = mnew;
+                lsum *= corr;
+#pragma unroll
+                for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) O[mt][i] *= corr;
+            }
+            const float mref = (m == -INFINITY) ? 0.f : m;
+            bf16x8_t P[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = exp2_fast(fmaf(S[s >> 1][8 * (s & 1) + e], scale_log2e, -mref));
+                    lsum += p[e];
+                }
+                uint4 u = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]),
+                                     pack2(p[6], p[7]));
+                P[s] = __builtin_bit_cast(bf16x8_t, u);
+            }
+            // O^T += V^T P^T: k = key in the permuted order of the S^T accumulators
+            const char *vt = cur + TL::KBYTES;
+#pragma unroll
+            for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int off = ((32 * mt + l32) * TL::VROW + 16 * s + 4 * h) * 2;
+                    bf16x4_t a0 = *reinterpret_cast<const bf16x4_t *>(vt + off);
+                    bf16x4_t a1 = *reinterpret_cast<const bf16x4_t *>(vt + off + 16);
+                    O[mt] = mfma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), P[s], O[mt]);
+                }
+        }
+        if (more) store_tile<D>(smem + (buf ^ 1) * TL::BYTES, rk, rv);
+        __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.f / ltot;
+    if (qi < T) {
+        bf16_t *op = o + ((size_t)bh * T + qi) * D;
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = 32 * mt + 8 * a4 + 4 * h;
+                *reinterpret_cast<uint2 *>(op + d0) =
+                    make_uint2(pack2(O[mt][4 * a4 + 0] * inv, O[mt][4 * a4 + 1] * inv),
+                               pack2(O[mt][4 * a4 + 2] * inv, O[mt][4 * a4 + 3] * inv));
+            }
+    }
+}
+
+}  // namespace
+
+bool swska_supported(int dk, int dv, int dtype) {
+    return dtype == 1 && dk == dv && (dk == 128 || dk == 64);
+}
+
+void launch_swska(const SkaArgs &a, hipStream_t st) {
+    const int BH = a.B * a.H;
+    const int nqb = (a.T + kBQ - 1) / kBQ;
+    const float sl2e = a.scale * kLog2e;
+    const int window = a.window < a.T ? a.window : a.T;  // w >= T: every earlier key
+    dim3 grid((unsigned)(BH * nqb));
+    if (a.dk == 128)
+        hipLaunchKernelGGL(swska_kernel<128>, grid, dim3(256), 0, st, (const bf16_t *)a.q,
+                           (const bf16_t *)a.k, (const bf16_t *)a.v, (bf16_t *)a.o, BH, a.H, a.T,
+                           window, sl2e, nqb);
+    else
+        hipLaunchKernelGGL(swska_kernel<64>, grid, dim3(256), 0, st, (const bf16_t *)a.q,
+                           (const bf16_t *)a.k, (const bf16_t *)a.v, (bf16_t *)a.o, BH, a.H, a.T,
+                           window, sl2e, nqb);
+}
 
 }  // namespace rodimus

@@ -71,6 +71,10 @@ def test_workspace_query():
     n = rd.rodimus_scan_prefill_workspace_bytes(1, 16, 131072, 128, 128, 64, rd.BF16)
     assert n >= 0
     assert rd.rodimus_scan_prefill_workspace_bytes(4, 16, 4096, 128, 128, 0, rd.BF16) >= 0
+    # empty problems need no workspace (and must not divide by zero)
+    assert rd.rodimus_scan_prefill_workspace_bytes(2, 3, 0, 128, 128, 64, rd.BF16) == 0
+    assert rd.rodimus_scan_prefill_workspace_bytes(0, 3, 100, 128, 128, 64, rd.BF16) == 0
+    assert rd.rodimus_scan_prefill_workspace_bytes(1, 1, 1, 128, 128, 32, rd.BF16) == 0
 
 
 def decode(**kw):
