@@ -10,37 +10,42 @@
 //     Qt = q * 2^{Lam}                      (bf16 MFMA operand)
 //     Kh = k * 2^{log2 beta - Lam}          (bf16)
 //     Kb = Kh * 2^{Lam[C-1]}                (bf16)
-//     o  = Qt S  +  tril(Qt Kh^T) V         (two MFMA contractions, fp32 acc)
-//     S' = diag(2^{Lam[C-1]}) S + Kb^T V    (MFMA, fp32 acc, state in registers)
+//     o  = Qt S  +  tril(Qt Kh^T) V         (MFMA, fp32 accumulation)
+//     S' = diag(2^{Lam[C-1]}) S + Kb^T V    (MFMA, fp32 accumulation)
 //
-// A chunk whose decay span max_i(-Lam[C-1, i]) exceeds kSpan2 (where 2^{-Lam}
-// would leave the fp32/bf16 range) is instead processed token by token on the
-// VALU, which gives the same result.
+// Kh needs 2^{-Lam} to stay inside the fp32/bf16 range: a chunk whose decay
+// span max_i(-Lam[C-1, i]) exceeds kSpan2 is processed token by token on the
+// VALU instead (same result).  Kb never overflows (its exponent is <= 0).
 //
-// Work decomposition.  One workgroup of 4 waves runs one (b, h) pair over one
-// segment of the sequence.  Each wave owns 32 of the 128 state columns: the
-// fp32 state tile 128x32 stays in MFMA accumulator registers for the whole
-// segment and never goes through memory between chunks.  Per chunk:
-//   producer (all 256 lanes, VALU): gates, in-chunk scan of log2 a (DPP scan
-//     inside 16-lane rows), the operands Qt, Kh, Kb^T, V^T written to LDS;
-//   consumer (MFMA): wave w < C/32 + 1 builds one 32x32 tile of the masked
-//     score matrix; then every wave computes its o columns and its state slice.
-// The next chunk's raw inputs are loaded into registers while the current
-// chunk's contractions run.
+// Segment-parallel form.  So that the grid fills the GPU when B*H is small, the
+// sequence of each (b, h) is cut into G segments (each a whole number of
+// chunks), and every segment but the last into P sub-segments:
+//   phase 1 (scan_state_kernel): each sub-segment's local end state (from zero)
+//            and its total log2 decay.  Chunks are visited last to first, so the
+//            decay of the later chunks folds into the operand exponent:
+//            S_loc = sum_c (Kb_c * 2^{rho_c})^T V_c, rho_c = sum of Lam_end after c;
+//            there is no state rescaling and nothing can overflow;
+//   phase 2 (scan_combine_kernel): S_in of every segment, left to right;
+//   phase 3 (scan_full_kernel): every segment from its S_in, writing o.
 //
-// Long sequences with few (b, h) pairs are split into G segments so that the
-// grid fills the GPU (segment-parallel form of the same recurrence):
-//   phase 1 (STATE_ONLY): each segment but the last computes its local end
-//            state from zero and its total log2 decay;
-//   phase 2 (combine):   S_in[j+1] = diag(2^{A_j}) S_in[j] + S_loc[j], left to right;
-//   phase 3 (FULL):      each segment reruns from its S_in and writes o.
+// scan_full_kernel: 8 waves.  Waves 0-3 (producers) turn chunk k's raw inputs
+// into LDS operands (gates, DPP scan of log2 a inside 16-lane rows, Qt, Kh,
+// Kb^T, V^T) while waves 4-7 (consumers) contract chunk k-1 on the matrix cores
+// from the other LDS buffer; one barrier per chunk.  Each consumer wave owns 32
+// of the 128 state columns: its fp32 128x32 state slice lives in MFMA
+// accumulator registers for the whole segment.  The masked score tiles stay in
+// registers too: A^T = Kh Qt^T is built in accumulator layout, which is already
+// the operand layout of o^T += V^T A^T under a permuted k order.  o is produced
+// transposed (o^T = S^T Qt^T + V^T A^T) so that each lane stores 8-byte runs.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operand A[m][k] sits in lane m + 32*(k/8),
 // element k%8; B[k][n] in lane n + 32*(k/8), element k%8; the accumulator
-// C[m][n] in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.  The state kept in
-// accumulator layout feeds the o = Qt S contraction directly as operand B with
-// a permuted k order (rows 4h..4h+3 and 8+4h..8+4h+3 of each 16-row step); Qt
-// is read from LDS with the same permutation.
+// C[m][n] in lane n + 32*((m/4)%2), register 4*(m/8) + m%4.  An accumulator
+// therefore holds, per lane half h, the rows {4h..4h+3, 8+4h..8+4h+3} of every
+// 16-row step; used as an operand it contracts k in that order.  LDS stores
+// the channels of Qt/Kh and the tokens of Kb^T/V^T in the matching order
+// (blocks of 4 permuted as 0,2,1,3 inside each 16), so every operand read is
+// one 16-byte ds_read.
 #include "device_common.h"
 #include "launch.h"
 
@@ -48,34 +53,29 @@ namespace rodimus {
 
 namespace {
 
-constexpr int kD = 128;        // dk = dv
-constexpr int kThreads = 256;  // 4 waves
-constexpr float kSpan2 = 112.f;
-constexpr int kTargetBlocks = 256;  // one workgroup on each of the 256 CUs
+constexpr int kD = 128;            // dk = dv
+constexpr float kSpan2 = 112.f;    // 2^112 ~ 5e33: Kh stays finite in fp32/bf16
+constexpr int kCUs = 256;
+constexpr int kMaxT = 1 << 23;     // 32-bit buffer offsets (T * 256 bytes)
 
-// LDS layout (bytes).  Rows are padded by 16 bytes so that the 32 rows read by
-// one MFMA operand load fall in distinct banks.
-constexpr int kQRow = kD + 8;       // bf16 elements per row of sQ / sK  [C][128]
-constexpr int kTRow = 64 + 8;       // bf16 elements per row of sKbT / sVT [128][C]
-constexpr int kARow = 64 + 8;       // bf16 elements per row of sA [C][C]
+// LDS buffer layout (bytes); rows padded by 16 bytes (conflict-free 16-byte reads)
+constexpr int kQRow = kD + 8;      // bf16 per row of sQ / sK       [C][128]
+constexpr int kTRow = 64 + 8;      // bf16 per row of sKbT / sVT    [128][C]
 constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 64 * kQRow * 2;
 constexpr int kOffKbT = kOffK + 64 * kQRow * 2;
 constexpr int kOffVT = kOffKbT + kD * kTRow * 2;
-constexpr int kOffA = kOffVT + kD * kTRow * 2;
-constexpr int kOffGam = kOffA + 64 * kARow * 2;
-constexpr int kOffFlag = kOffGam + kD * 4;
-constexpr int kSmemBytes = kOffFlag + 16;
-static_assert(kSmemBytes <= 81920, "two workgroups per CU must fit in 160 KiB of LDS");
+constexpr int kOffGam = kOffVT + kD * kTRow * 2;
+constexpr int kBufBytes = kOffGam + kD * 4;
 
 struct Params {
     const bf16_t *q, *k, *v, *g, *th;
     const float *S0;  // [BH][128][128] or null (zeros)
     bf16_t *o;
     float *S_T;       // [BH][128][128] or null
-    float *wsS;       // [G-1][BH][128][128]: local end states, then incoming states
-    float *wsA;       // [G-1][BH][128]: total log2 decay of each segment
-    int BH, T, G, seg_len;
+    float *wsS;       // [(G-1)*P][BH][128][128] sub-segment states / incoming states
+    float *wsA;       // [(G-1)*P][BH][128] total log2 decay of each sub-segment
+    int BH, T, G, seg_len, P, sub_len;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -83,447 +83,559 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     f32x2_t f = {a, b};
-    bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, h);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
-
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
 __device__ __forceinline__ void unpack8(const uint4 &x, float *f) {
-    f[0] = lo_bf(x.x); f[1] = hi_bf(x.x);
-    f[2] = lo_bf(x.y); f[3] = hi_bf(x.y);
-    f[4] = lo_bf(x.z); f[5] = hi_bf(x.z);
-    f[6] = lo_bf(x.w); f[7] = hi_bf(x.w);
+    f[0] = lo_bf(x.x); f[1] = hi_bf(x.x); f[2] = lo_bf(x.y); f[3] = hi_bf(x.y);
+    f[4] = lo_bf(x.z); f[5] = hi_bf(x.z); f[6] = lo_bf(x.w); f[7] = hi_bf(x.w);
 }
 
-// Shift right by k lanes inside each 16-lane row; lanes with no source get 0.
 template <int K>
-__device__ __forceinline__ float row_shr(float x) {
+__device__ __forceinline__ float row_shr(float x) {  // lane i <- lane i-K inside 16-lane rows, else 0
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                  0x110 + K, 0xf, 0xf, false));
 }
-
-__device__ __forceinline__ float bcast_lane(float x, int src_lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, x)));
+__device__ __forceinline__ float bcast_lane(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
-
 __device__ __forceinline__ f32x16_t mfma(const bf16x8_t &a, const bf16x8_t &b, const f32x16_t &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-
-__device__ __forceinline__ bf16x8_t lds_b128(const char *smem, int byte_off) {
-    return *reinterpret_cast<const bf16x8_t *>(smem + byte_off);
+__device__ __forceinline__ bf16x8_t lds16(const char *base, int byte_off) {
+    return *reinterpret_cast<const bf16x8_t *>(base + byte_off);
 }
-
-__device__ __forceinline__ bf16x8_t lds_2x_b64(const char *smem, int off0, int off1) {
-    bf16x4_t a = *reinterpret_cast<const bf16x4_t *>(smem + off0);
-    bf16x4_t b = *reinterpret_cast<const bf16x4_t *>(smem + off1);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
+// 8 accumulator registers [base, base+8) as a bf16 operand
 __device__ __forceinline__ bf16x8_t cvt8(const f32x16_t &s, int base) {
-    uint4 u;
-    u.x = pack2(s[base + 0], s[base + 1]);
-    u.y = pack2(s[base + 2], s[base + 3]);
-    u.z = pack2(s[base + 4], s[base + 5]);
-    u.w = pack2(s[base + 6], s[base + 7]);
+    uint4 u = make_uint4(pack2(s[base + 0], s[base + 1]), pack2(s[base + 2], s[base + 3]),
+                         pack2(s[base + 4], s[base + 5]), pack2(s[base + 6], s[base + 7]));
     return __builtin_bit_cast(bf16x8_t, u);
 }
+// Position of index x in the permuted order (blocks of 4 placed 0,2,1,3 in each 16).
+__device__ __forceinline__ int perm16(int x) {
+    const int blk = (x >> 2) & 3;
+    return (x & ~15) | (((blk & 1) << 1 | (blk >> 1)) << 2) | (x & 3);
+}
 
-// One chunk of raw inputs held in registers by a producer lane: TPR tokens x 8
-// channels of each tensor (16-byte vectors).
-template <int TPR, bool FULL>
+// Workgroup-uniform values computed with integer division end up in vector
+// registers; readfirstlane moves them to scalar registers so that buffer
+// descriptors are scalar (no per-lane waterfall loops).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const bf16_t *uni_ptr(const bf16_t *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<const bf16_t *>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16_t *base, int T) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)uni_ptr(base), (short)0, uni(T * kD * 2), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// ------------------------------------------------------------------ producer
+// Producer lane (256 of them): channel group cg (channels 8cg..8cg+7) and
+// token group r (tokens TPR*r .. TPR*r+TPR-1); the 16 lanes of a DPP row
+// share cg and together cover the C tokens of the chunk.
+template <int C, bool WITH_Q>
 struct Raw {
-    uint4 q[FULL ? TPR : 1], k[TPR], g[TPR], th[TPR], v[TPR];
+    static constexpr int TPR = C / 16;
+    uint4 q[WITH_Q ? TPR : 1], k[TPR], g[TPR], th[TPR], v[TPR];
 };
 
-template <int C, bool FULL>
-__device__ __forceinline__ void load_raw(Raw<C / 16, FULL> &R, const Params &p, size_t rowbase,
-                                         int t0, int tend, int r, int cg) {
+struct Rsrc {
+    __amdgpu_buffer_rsrc_t q, k, v, g, th;
+};
+
+// Loads past T read zeros (buffer bounds).
+template <int C, bool WITH_Q>
+__device__ __forceinline__ void load_raw(Raw<C, WITH_Q> &R, const Rsrc &rs, int t0, int r, int cg) {
     constexpr int TPR = C / 16;
 #pragma unroll
     for (int tt = 0; tt < TPR; ++tt) {
-        const int t = t0 + TPR * r + tt;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        if (t < tend) {
-            const size_t e = (rowbase + t) * kD + 8 * cg;
-            if (FULL) R.q[tt] = *reinterpret_cast<const uint4 *>(p.q + e);
-            R.k[tt] = *reinterpret_cast<const uint4 *>(p.k + e);
-            R.g[tt] = *reinterpret_cast<const uint4 *>(p.g + e);
-            R.th[tt] = *reinterpret_cast<const uint4 *>(p.th + e);
-            R.v[tt] = *reinterpret_cast<const uint4 *>(p.v + e);
-        } else {
-            if (FULL) R.q[tt] = z;
-            R.k[tt] = z; R.g[tt] = z; R.th[tt] = z; R.v[tt] = z;
-        }
+        const int off = (t0 + TPR * r + tt) * (kD * 2) + 16 * cg;
+        if (WITH_Q) R.q[tt] = bload(rs.q, off);
+        R.k[tt] = bload(rs.k, off);
+        R.g[tt] = bload(rs.g, off);
+        R.th[tt] = bload(rs.th, off);
+        R.v[tt] = bload(rs.v, off);
     }
 }
 
-// Token-by-token processing of one chunk (decay span too large for the
-// factorised form).  Uses the operand area of LDS as fp32 scratch.
-template <int C, bool FULL>
-__device__ void chunk_fallback(char *smem, const Params &p, size_t rowbase, int t0, int tend,
-                               f32x16_t (&S)[4], int bh) {
-    float *fa = reinterpret_cast<float *>(smem);   // [16][128] a
-    float *fb = fa + 16 * kD;                      // [16][128] beta*k
-    float *fq = fb + 16 * kD;                      // [16][128] q
-    float *fv = fq + 16 * kD;                      // [16][128] v
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, n = 32 * w + (l & 31);
-    for (int sb = 0; sb < C; sb += 16) {
-        __syncthreads();
-        for (int e = tid; e < 16 * kD; e += kThreads) {
-            const int tt = e / kD, i = e % kD, t = t0 + sb + tt;
-            float a = 1.f, bk = 0.f, qq = 0.f, vv = 0.f;
-            if (t < tend) {
-                const size_t x = (rowbase + t) * kD + i;
-                float l2a, l2b;
-                ddts_log2_gates(bf2f(p.g[x]), bf2f(p.th[x]), l2a, l2b);
-                a = exp2_fast(l2a);
-                bk = exp2_fast(l2b) * bf2f(p.k[x]);
-                if (FULL) qq = bf2f(p.q[x]);
-                vv = bf2f(p.v[x]);
-            }
-            fa[e] = a; fb[e] = bk; fq[e] = qq; fv[e] = vv;
-        }
-        __syncthreads();
-        for (int tt = 0; tt < 16; ++tt) {
-            const int t = t0 + sb + tt;
-            if (t >= tend) break;
-            const float vn = fv[tt * kD + n];
-            float part = 0.f;
+// One tensor's TPR vectors of chunk t0 (for prefetching each tensor right
+// after the last use of its registers).
+template <int TPR>
+__device__ __forceinline__ void load_one(uint4 (&x)[TPR], __amdgpu_buffer_rsrc_t rs, int t0, int r, int cg) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+    for (int tt = 0; tt < TPR; ++tt) x[tt] = bload(rs, (t0 + TPR * r + tt) * (kD * 2) + 16 * cg);
+}
+
+// Gates and in-chunk inclusive scan: on return l2a holds Lam (inclusive
+// cumulative log2 a), l2b log2 beta, lend the chunk total Lam[C-1] of each of
+// the lane's 8 channels.  Tokens at or beyond tend get a = 1, beta = 0.
+template <int C, bool WITH_Q>
+__device__ __forceinline__ void gates_scan(const Raw<C, WITH_Q> &R, int t0, int tend, int r, int l,
+                                           float (&l2a)[C / 16][8], float (&l2b)[C / 16][8],
+                                           float (&lend)[8]) {
+    constexpr int TPR = C / 16;
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const int i0 = 32 * mt + 8 * a4 + 4 * h;
-                    const float4 av = *reinterpret_cast<const float4 *>(fa + tt * kD + i0);
-                    const float4 bv = *reinterpret_cast<const float4 *>(fb + tt * kD + i0);
-                    const float4 qv = *reinterpret_cast<const float4 *>(fq + tt * kD + i0);
-                    float x;
-                    x = fmaf(av.x, S[mt][4 * a4 + 0], bv.x * vn); S[mt][4 * a4 + 0] = x; part = fmaf(qv.x, x, part);
-                    x = fmaf(av.y, S[mt][4 * a4 + 1], bv.y * vn); S[mt][4 * a4 + 1] = x; part = fmaf(qv.y, x, part);
-                    x = fmaf(av.z, S[mt][4 * a4 + 2], bv.z * vn); S[mt][4 * a4 + 2] = x; part = fmaf(qv.z, x, part);
-                    x = fmaf(av.w, S[mt][4 * a4 + 3], bv.w * vn); S[mt][4 * a4 + 3] = x; part = fmaf(qv.w, x, part);
-                }
+    for (int tt = 0; tt < TPR; ++tt) {
+        float gf[8], tf[8];
+        unpack8(R.g[tt], gf);
+        unpack8(R.th[tt], tf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ddts_log2_gates_fast(gf[e], tf[e], l2a[tt][e], l2b[tt][e]);
+    }
+    if (t0 + C > tend) {  // ragged last chunk
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt)
+            if (t0 + TPR * r + tt >= tend) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { l2a[tt][e] = 0.f; l2b[tt][e] = -INFINITY; }
             }
-            if (FULL) {
-                part += __shfl_xor(part, 32);
-                if (h == 0) p.o[((size_t)bh * p.T + t) * kD + n] = f2bf(part);
-            }
-        }
+    }
+#pragma unroll
+    for (int tt = 1; tt < TPR; ++tt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l2a[tt][e] += l2a[tt - 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float x = l2a[TPR - 1][e];
+        x += row_shr<1>(x);
+        x += row_shr<2>(x);
+        x += row_shr<4>(x);
+        x += row_shr<8>(x);
+        const float excl = row_shr<1>(x);
+        lend[e] = bcast_lane(x, (l & 48) | 15);
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) l2a[tt][e] += excl;
     }
 }
 
-template <int C, bool FULL>
-__global__ __launch_bounds__(kThreads, 1)
-void scan_mfma_kernel(Params p) {
-    constexpr int TPR = C / 16;   // tokens per producer lane
-    constexpr int NT = C / 32;    // 32-token tiles per chunk
-    __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-    int *sFlag = reinterpret_cast<int *>(smem + kOffFlag);
-    float *sGam = reinterpret_cast<float *>(smem + kOffGam);
+// Row c of Kb^T / V^T: tokens TPR*r .. TPR*r+TPR-1 at their permuted position.
+template <int TPR>
+__device__ __forceinline__ void store_t_rows(char *base, int c, int r, const float *x) {
+    char *p = base + (c * kTRow + perm16(TPR * r)) * 2;
+    if (TPR == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(pack2(x[0], x[1 % TPR]), pack2(x[2 % TPR], x[3 % TPR]));
+    else *reinterpret_cast<uint32_t *>(p) = pack2(x[0], x[1 % TPR]);
+}
+// V^T rows 8cg..8cg+7 straight from the raw bf16 registers (no conversion).
+template <int TPR>
+__device__ __forceinline__ void store_vt(char *base, int cg, int r, const uint4 (&v)[TPR]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t w[TPR];
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) {
+            const uint32_t word = (e < 2) ? v[tt].x : (e < 4) ? v[tt].y : (e < 6) ? v[tt].z : v[tt].w;
+            w[tt] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        }
+        char *p = base + ((8 * cg + e) * kTRow + perm16(TPR * r)) * 2;
+        if (TPR == 4) *reinterpret_cast<uint2 *>(p) = make_uint2(w[0] | (w[1 % TPR] << 16), w[2 % TPR] | (w[3 % TPR] << 16));
+        else *reinterpret_cast<uint32_t *>(p) = w[0] | (w[1 % TPR] << 16);
+    }
+}
+
+// Channels 8cg..8cg+7 of token row t of Qt / Kh at their permuted positions.
+__device__ __forceinline__ void store_q_row(char *base, int t, int cg, const float *x) {
+    char *p = base + (t * kQRow) * 2;
+    *reinterpret_cast<uint2 *>(p + perm16(8 * cg) * 2) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+    *reinterpret_cast<uint2 *>(p + perm16(8 * cg + 4) * 2) = make_uint2(pack2(x[4], x[5]), pack2(x[6], x[7]));
+}
+
+// ------------------------------------------------------------- phase 3 (full)
+template <int C>
+__global__ __launch_bounds__(512, 1)
+void scan_full_kernel(Params p) {
+    constexpr int TPR = C / 16, NT = C / 32;
+    __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + 16];
+    int *sFlag = reinterpret_cast<int *>(smem + 2 * kBufBytes);  // chunk k -> slot k % 3
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-    // producer coordinates: token group r (TPR consecutive tokens), channel group cg (8 channels)
-    const int r = l & 15, cg = (w << 2) | (l >> 4);
-
-    const int nseg = FULL ? p.G : p.G - 1;
-    const int bh = blockIdx.x % p.BH, seg = blockIdx.x / p.BH;
-    if (seg >= nseg) return;
+    const int bh = uni(blockIdx.x % p.BH), seg = uni(blockIdx.x / p.BH);
+    if (seg >= p.G) return;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.T, t_begin + p.seg_len);
+    const int nch = (t_end - t_begin + C - 1) / C;
     const size_t rowbase = (size_t)bh * p.T;
-    const size_t sstride = (size_t)kD * kD;
 
-    // ---- initial state (accumulator layout): rows 32mt + 8a + 4h + r4, column 32w + l32
-    f32x16_t S[4];
-    const float *Sin = nullptr;
-    if (FULL) Sin = (seg == 0) ? (p.S0 ? p.S0 + bh * sstride : nullptr)
-                               : p.wsS + ((size_t)(seg - 1) * p.BH + bh) * sstride;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-            S[mt][i] = Sin ? Sin[row * kD + 32 * w + l32] : 0.f;
-        }
-
-    float logdecay[8];  // running sum of this lane's 8 channels' Lam_end (STATE_ONLY)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) logdecay[e] = 0.f;
-
-    if (tid < 2) sFlag[tid] = 0;
+    if (tid < 3) sFlag[tid] = 0;
     __syncthreads();
 
-    Raw<TPR, FULL> R;
-    load_raw<C, FULL>(R, p, rowbase, t_begin, t_end, r, cg);
-
-    int parity = 0;
-    for (int t0 = t_begin; t0 < t_end; t0 += C, parity ^= 1) {
-        // ================= producer: gates, scan, operands -> LDS =================
-        {
-            float l2a[TPR][8], l2b[TPR][8];
-#pragma unroll
-            for (int tt = 0; tt < TPR; ++tt) {
-                float gf[8], tf[8];
-                unpack8(R.g[tt], gf);
-                unpack8(R.th[tt], tf);
-                const bool valid = (t0 + TPR * r + tt) < t_end;
+    if (w < 4) {
+        // ======================= producers =======================
+        const int r = l & 15, cg = (w << 2) | (l >> 4);
+        Rsrc rs;
+        rs.q = rsrc(p.q + rowbase * kD, p.T); rs.k = rsrc(p.k + rowbase * kD, p.T);
+        rs.v = rsrc(p.v + rowbase * kD, p.T); rs.g = rsrc(p.g + rowbase * kD, p.T);
+        rs.th = rsrc(p.th + rowbase * kD, p.T);
+        Raw<C, true> R;
+        load_raw<C, true>(R, rs, t_begin, r, cg);
+        for (int kk = 0; kk <= nch; ++kk) {
+            if (kk < nch) {
+                const int t0 = t_begin + kk * C;
+                char *buf = smem + (kk & 1) * kBufBytes;
+                const bool more = kk + 1 < nch;
+                store_vt<TPR>(buf + kOffVT, cg, r, R.v);
+                if (more) load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
+                float l2a[TPR][8], l2b[TPR][8], lend[8];
+                gates_scan<C, true>(R, t0, t_end, r, l, l2a, l2b, lend);
+                if (more) {
+                    load_one<TPR>(R.g, rs.g, t0 + C, r, cg);
+                    load_one<TPR>(R.th, rs.th, t0 + C, r, cg);
+                }
+                bool bad = false;
+                float gam[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    ddts_log2_gates_fast(gf[e], tf[e], l2a[tt][e], l2b[tt][e]);
-                    if (!valid) { l2a[tt][e] = 0.f; l2b[tt][e] = -INFINITY; }
+                    bad |= lend[e] < -kSpan2;
+                    gam[e] = exp2_fast(lend[e]);
                 }
-            }
-            // in-lane inclusive scan over the TPR tokens
-#pragma unroll
-            for (int tt = 1; tt < TPR; ++tt)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) l2a[tt][e] += l2a[tt - 1][e];
-            // scan of the per-lane totals across the 16 lanes of the row
-            float excl[8], lend[8];
-            bool bad = false;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = l2a[TPR - 1][e];
-                x += row_shr<1>(x);
-                x += row_shr<2>(x);
-                x += row_shr<4>(x);
-                x += row_shr<8>(x);
-                excl[e] = row_shr<1>(x);
-                lend[e] = bcast_lane(x, (l & 48) | 15);
-                bad |= lend[e] < -kSpan2;
-                logdecay[e] += lend[e];
-            }
-            float gam[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) gam[e] = exp2_fast(lend[e]);
-            if (r == 0) {
-                *reinterpret_cast<float4 *>(sGam + 8 * cg) = make_float4(gam[0], gam[1], gam[2], gam[3]);
-                *reinterpret_cast<float4 *>(sGam + 8 * cg + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
-            }
-            if (bad) sFlag[parity] = 1;
-
-            float kb[TPR][8], vf[TPR][8];
-#pragma unroll
-            for (int tt = 0; tt < TPR; ++tt) {
-                const int t = TPR * r + tt;  // token index inside the chunk
-                float kf[8];
-                unpack8(R.k[tt], kf);
-                unpack8(R.v[tt], vf[tt]);
-                float kh[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float lam = l2a[tt][e] + excl[e];
-                    kh[e] = kf[e] * exp2_fast(l2b[tt][e] - lam);
-                    kb[tt][e] = kh[e] * gam[e];
-                    l2a[tt][e] = lam;
+                if (r == 0) {
+                    float *sg = reinterpret_cast<float *>(buf + kOffGam) + 8 * cg;
+                    *reinterpret_cast<float4 *>(sg) = make_float4(gam[0], gam[1], gam[2], gam[3]);
+                    *reinterpret_cast<float4 *>(sg + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
                 }
-                if (FULL) {
-                    float qf[8], qt[8];
+                if (bad) sFlag[kk % 3] = 1;
+                if (tid == 0) sFlag[(kk + 1) % 3] = 0;
+                float kbT[8][TPR];
+#pragma unroll
+                for (int tt = 0; tt < TPR; ++tt) {
+                    float qf[8], kf[8], qt[8], kh[8];
                     unpack8(R.q[tt], qf);
+                    unpack8(R.k[tt], kf);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) qt[e] = qf[e] * exp2_fast(l2a[tt][e]);
-                    uint4 uq = make_uint4(pack2(qt[0], qt[1]), pack2(qt[2], qt[3]),
-                                          pack2(qt[4], qt[5]), pack2(qt[6], qt[7]));
-                    uint4 uk = make_uint4(pack2(kh[0], kh[1]), pack2(kh[2], kh[3]),
-                                          pack2(kh[4], kh[5]), pack2(kh[6], kh[7]));
-                    *reinterpret_cast<uint4 *>(smem + kOffQ + (t * kQRow + 8 * cg) * 2) = uq;
-                    *reinterpret_cast<uint4 *>(smem + kOffK + (t * kQRow + 8 * cg) * 2) = uk;
-                }
-            }
-            // transposed Kb and V: row = channel, TPR consecutive tokens per write
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 8 * cg + e;
-                if (TPR == 4) {
-                    uint2 ukb = make_uint2(pack2(kb[0][e], kb[1 % TPR][e]), pack2(kb[2 % TPR][e], kb[3 % TPR][e]));
-                    uint2 uvv = make_uint2(pack2(vf[0][e], vf[1 % TPR][e]), pack2(vf[2 % TPR][e], vf[3 % TPR][e]));
-                    *reinterpret_cast<uint2 *>(smem + kOffKbT + (c * kTRow + TPR * r) * 2) = ukb;
-                    *reinterpret_cast<uint2 *>(smem + kOffVT + (c * kTRow + TPR * r) * 2) = uvv;
-                } else {
-                    *reinterpret_cast<uint32_t *>(smem + kOffKbT + (c * kTRow + TPR * r) * 2) = pack2(kb[0][e], kb[1 % TPR][e]);
-                    *reinterpret_cast<uint32_t *>(smem + kOffVT + (c * kTRow + TPR * r) * 2) = pack2(vf[0][e], vf[1 % TPR][e]);
-                }
-            }
-        }
-        __syncthreads();  // operands of this chunk are in LDS
-
-        // prefetch the next chunk's raw inputs while the contractions run
-        if (t0 + C < t_end) load_raw<C, FULL>(R, p, rowbase, t0 + C, t_end, r, cg);
-        if (tid == 0) sFlag[parity ^ 1] = 0;
-
-        if (sFlag[parity]) {
-            chunk_fallback<C, FULL>(smem, p, rowbase, t0, t_end, S, bh);
-            __syncthreads();
-            continue;
-        }
-
-        // ================= consumer: MFMA contractions =================
-        // V^T operand fragments (B operand, k = token): reused by o and by the state update
-        bf16x8_t vB[C / 16];
-#pragma unroll
-        for (int s = 0; s < C / 16; ++s)
-            vB[s] = lds_b128(smem, kOffVT + ((32 * w + l32) * kTRow + 16 * s + 8 * h) * 2);
-
-        if (FULL) {
-            // (1) masked score tiles A^T[j][i] = Kh[j] . Qt[i], j <= i; wave w builds tile w
-            //     (Jt, It) in {(0,0), (0,1), (1,1)} for C = 64, {(0,0)} for C = 32.
-            if (w < (NT == 2 ? 3 : 1)) {
-                const int Jt = (w == 2) ? 1 : 0;
-                const int It = (w == 0) ? 0 : 1;
-                f32x16_t acc = {};
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    bf16x8_t a = lds_b128(smem, kOffK + ((32 * Jt + l32) * kQRow + 16 * s + 8 * h) * 2);
-                    bf16x8_t b = lds_b128(smem, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2);
-                    acc = mfma(a, b, acc);
-                }
-                const int i = 32 * It + l32;
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    float x[4];
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int j = 32 * Jt + 8 * a4 + 4 * h + r4;
-                        x[r4] = (j <= i) ? acc[4 * a4 + r4] : 0.f;
+                    for (int e = 0; e < 8; ++e) {
+                        qt[e] = qf[e] * exp2_fast(l2a[tt][e]);
+                        kh[e] = kf[e] * exp2_fast(l2b[tt][e] - l2a[tt][e]);
+                        kbT[e][tt] = kh[e] * gam[e];
                     }
-                    *reinterpret_cast<uint2 *>(smem + kOffA + (i * kARow + 32 * Jt + 8 * a4 + 4 * h) * 2) =
-                        make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+                    const int t = TPR * r + tt;
+                    store_q_row(buf + kOffQ, t, cg, qt);
+                    store_q_row(buf + kOffK, t, cg, kh);
                 }
+                if (more) {
+                    load_one<TPR>(R.q, rs.q, t0 + C, r, cg);
+                    load_one<TPR>(R.k, rs.k, t0 + C, r, cg);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) store_t_rows<TPR>(buf + kOffKbT, 8 * cg + e, r, kbT[e]);
             }
-            // bf16 copy of the state for o = Qt S (operand B, permuted k order)
-            bf16x8_t Sb[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Sb[s] = cvt8(S[s >> 1], 8 * (s & 1));
-            __syncthreads();  // score tiles ready
-
-            // (2) o tiles for this wave's 32 columns
-#pragma unroll
-            for (int It = 0; It < NT; ++It) {
-                f32x16_t acc = {};
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int rowoff = (32 * It + l32) * kQRow + 16 * s + 4 * h;
-                    bf16x8_t a = lds_2x_b64(smem, kOffQ + rowoff * 2, kOffQ + (rowoff + 8) * 2);
-                    acc = mfma(a, Sb[s], acc);
-                }
-#pragma unroll
-                for (int s = 0; s < 2 * It + 2; ++s) {
-                    bf16x8_t a = lds_b128(smem, kOffA + ((32 * It + l32) * kARow + 16 * s + 8 * h) * 2);
-                    acc = mfma(a, vB[s], acc);
-                }
-                const int n = 32 * w + l32;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = t0 + 32 * It + 8 * (i >> 2) + 4 * h + (i & 3);
-                    if (t < t_end) p.o[(rowbase + t) * kD + n] = f2bf(acc[i]);
-                }
-            }
+            __syncthreads();
         }
-
-        // (3) state: S <- diag(gamma) S + Kb^T V  (this wave's 32 columns)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const float4 gm = *reinterpret_cast<const float4 *>(sGam + 32 * mt + 8 * a4 + 4 * h);
-                S[mt][4 * a4 + 0] *= gm.x;
-                S[mt][4 * a4 + 1] *= gm.y;
-                S[mt][4 * a4 + 2] *= gm.z;
-                S[mt][4 * a4 + 3] *= gm.w;
-            }
-#pragma unroll
-            for (int s = 0; s < C / 16; ++s) {
-                bf16x8_t a = lds_b128(smem, kOffKbT + ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2);
-                S[mt] = mfma(a, vB[s], S[mt]);
-            }
-        }
-        __syncthreads();  // LDS operands free for the next chunk
+        return;
     }
 
-    // ---- outputs of the segment
-    float *Sout = nullptr;
-    if (FULL) {
-        if (seg == p.G - 1) Sout = p.S_T ? p.S_T + bh * sstride : nullptr;
-    } else {
-        Sout = p.wsS + ((size_t)seg * p.BH + bh) * sstride;
-        if (r == 0) {
-            float *A = p.wsA + ((size_t)seg * p.BH + bh) * kD + 8 * cg;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) A[e] = logdecay[e];
-        }
-    }
-    if (Sout) {
+    // ======================= consumers =======================
+    const int cw = w - 4;                 // state columns 32cw .. 32cw+31
+    const int n = 32 * cw + l32;
+    f32x16_t S[4];                        // rows 32mt + 8a + 4h + r4, column n
+    {
+        const float *Sin = (seg == 0) ? (p.S0 ? p.S0 + (size_t)bh * kD * kD : nullptr)
+                                      : p.wsS + ((size_t)(seg * p.P - 1) * p.BH + bh) * kD * kD;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-                Sout[row * kD + 32 * w + l32] = S[mt][i];
+            for (int i = 0; i < 16; ++i)
+                S[mt][i] = Sin ? Sin[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + n] : 0.f;
+    }
+    for (int kk = 0; kk <= nch; ++kk) {
+        if (kk >= 1) {
+            const int c = kk - 1;
+            const int t0 = t_begin + c * C;
+            char *buf = smem + (c & 1) * kBufBytes;
+            if (sFlag[c % 3]) {
+                // Token-by-token fallback.  Each consumer wave works alone in a
+                // private 6 KiB slice of this chunk's (no longer needed) buffer.
+                float *fa = reinterpret_cast<float *>(buf) + cw * 1536;  // [4][128] a
+                float *fb = fa + 512;                                    // [4][128] beta*k
+                float *fq = fb + 512;                                    // [4][128] q
+                for (int sb = 0; sb < C; sb += 4) {
+                    for (int e = l; e < 512; e += 64) {
+                        const int tt = e >> 7, i = e & 127, t = t0 + sb + tt;
+                        float a = 1.f, bk = 0.f, qq = 0.f;
+                        if (t < t_end) {
+                            const size_t x = (rowbase + t) * kD + i;
+                            float l2a, l2b;
+                            ddts_log2_gates(bf2f(p.g[x]), bf2f(p.th[x]), l2a, l2b);
+                            a = exp2_fast(l2a);
+                            bk = exp2_fast(l2b) * bf2f(p.k[x]);
+                            qq = bf2f(p.q[x]);
+                        }
+                        fa[e] = a; fb[e] = bk; fq[e] = qq;
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    for (int tt = 0; tt < 4; ++tt) {
+                        const int t = t0 + sb + tt;
+                        if (t >= t_end) break;
+                        const float vn = bf2f(p.v[(rowbase + t) * kD + n]);
+                        float part = 0.f;
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                            for (int a4 = 0; a4 < 4; ++a4) {
+                                const int i0 = tt * 128 + 32 * mt + 8 * a4 + 4 * h;
+                                const float4 av = *reinterpret_cast<const float4 *>(fa + i0);
+                                const float4 bv = *reinterpret_cast<const float4 *>(fb + i0);
+                                const float4 qv = *reinterpret_cast<const float4 *>(fq + i0);
+                                float x;
+                                x = fmaf(av.x, S[mt][4 * a4 + 0], bv.x * vn); S[mt][4 * a4 + 0] = x; part = fmaf(qv.x, x, part);
+                                x = fmaf(av.y, S[mt][4 * a4 + 1], bv.y * vn); S[mt][4 * a4 + 1] = x; part = fmaf(qv.y, x, part);
+                                x = fmaf(av.z, S[mt][4 * a4 + 2], bv.z * vn); S[mt][4 * a4 + 2] = x; part = fmaf(qv.z, x, part);
+                                x = fmaf(av.w, S[mt][4 * a4 + 3], bv.w * vn); S[mt][4 * a4 + 3] = x; part = fmaf(qv.w, x, part);
+                            }
+                        part += __shfl_xor(part, 32);
+                        if (h == 0) p.o[(rowbase + t) * kD + n] = f2bf(part);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                }
+            } else {
+                // V^T fragments: B operand (k = token, permuted order) of both
+                // o += A V and S += Kb^T V
+                bf16x8_t vB[C / 16];
+#pragma unroll
+                for (int s = 0; s < C / 16; ++s)
+                    vB[s] = lds16(buf, kOffVT + (n * kTRow + 16 * s + 8 * h) * 2);
+                // bf16 state as the B operand of o += Qt S (k = channel, permuted order)
+                bf16x8_t Sb[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) Sb[s] = cvt8(S[s >> 1], 8 * (s & 1));
+                // masked score tiles A^T[j][i] = Kh[j] . Qt[i] (j <= i), accumulator layout;
+                // (Jt, It) = (0,0), (0,1), (1,1), only the first for C = 32
+                f32x16_t At[NT == 2 ? 3 : 1];
+#pragma unroll
+                for (int ti = 0; ti < (NT == 2 ? 3 : 1); ++ti) {
+                    const int Jt = (ti == 2) ? 1 : 0, It = (ti == 0) ? 0 : 1;
+                    At[ti] = f32x16_t{};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const bf16x8_t a = lds16(buf, kOffK + ((32 * Jt + l32) * kQRow + 16 * s + 8 * h) * 2);
+                        const bf16x8_t b = lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2);
+                        At[ti] = mfma(a, b, At[ti]);
+                    }
+                    if (Jt == It) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (8 * (i >> 2) + 4 * h + (i & 3) > l32) At[ti][i] = 0.f;
+                    }
+                }
+                // o^T tiles: 32 value channels (this wave's) x 32 tokens (32It..).  Same
+                // fragments as o = Qt S + A V with the operands swapped, so that a
+                // lane holds one token and 4 consecutive channels per register group.
+#pragma unroll
+                for (int It = 0; It < NT; ++It) {
+                    f32x16_t acc = {};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s)
+                        acc = mfma(Sb[s], lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2), acc);
+#pragma unroll
+                    for (int s = 0; s < 2 * It + 2; ++s) {
+                        const int ti = (It == 0) ? 0 : (s < 2 ? 1 : 2);
+                        acc = mfma(vB[s], cvt8(At[ti], 8 * (s & 1)), acc);
+                    }
+                    const int t = t0 + 32 * It + l32;
+                    if (t < t_end) {
+                        bf16_t *op = p.o + (rowbase + t) * kD + 32 * cw + 4 * h;
+#pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4)
+                            *reinterpret_cast<uint2 *>(op + 8 * a4) =
+                                make_uint2(pack2(acc[4 * a4 + 0], acc[4 * a4 + 1]),
+                                           pack2(acc[4 * a4 + 2], acc[4 * a4 + 3]));
+                    }
+                }
+                // state: S <- diag(gamma) S + Kb^T V
+                const float *gam = reinterpret_cast<const float *>(buf + kOffGam);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const float4 gm = *reinterpret_cast<const float4 *>(gam + 32 * mt + 8 * a4 + 4 * h);
+                        S[mt][4 * a4 + 0] *= gm.x; S[mt][4 * a4 + 1] *= gm.y;
+                        S[mt][4 * a4 + 2] *= gm.z; S[mt][4 * a4 + 3] *= gm.w;
+                    }
+#pragma unroll
+                    for (int s = 0; s < C / 16; ++s)
+                        S[mt] = mfma(lds16(buf, kOffKbT + ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
+                }
             }
+        }
+        __syncthreads();
+    }
+    if (seg == p.G - 1 && p.S_T) {
+        float *So = p.S_T + (size_t)bh * kD * kD;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) So[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + n] = S[mt][i];
     }
 }
 
-// Phase 2: S_in of segment j+1 = diag(2^{A_j}) S_in of segment j + S_loc[j], in place
-// over the local states.  One thread per (b,h, state element).
+// ----------------------------------------------------------- phase 1 (state)
+template <int C>
+__global__ __launch_bounds__(256, 2)
+void scan_state_kernel(Params p) {
+    constexpr int TPR = C / 16;
+    __shared__ __attribute__((aligned(16))) char smem[2 * kD * kTRow * 2];
+    char *sKbT = smem, *sVT = smem + kD * kTRow * 2;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+    const int nsub = (p.G - 1) * p.P;
+    const int bh = uni(blockIdx.x % p.BH), sub = uni(blockIdx.x / p.BH);
+    if (sub >= nsub) return;
+    const int seg = sub / p.P, part = sub % p.P;
+    const int seg_begin = seg * p.seg_len;
+    const int t_begin = seg_begin + part * p.sub_len;
+    const int t_end = min(seg_begin + p.seg_len, t_begin + p.sub_len);  // whole chunks
+    const int nch = (t_end - t_begin) / C;
+    const size_t rowbase = (size_t)bh * p.T;
+    const int r = l & 15, cg = (w << 2) | (l >> 4);
+
+    Rsrc rs;
+    rs.k = rsrc(p.k + rowbase * kD, p.T); rs.v = rsrc(p.v + rowbase * kD, p.T);
+    rs.g = rsrc(p.g + rowbase * kD, p.T); rs.th = rsrc(p.th + rowbase * kD, p.T);
+    rs.q = rs.k;
+
+    f32x16_t S[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) S[mt] = f32x16_t{};
+    float rho[8];  // log2 decay of the chunks after the current one, per channel
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rho[e] = 0.f;
+
+    Raw<C, false> R;
+    load_raw<C, false>(R, rs, t_begin + (nch - 1) * C, r, cg);
+    for (int c = nch - 1; c >= 0; --c) {
+        const int t0 = t_begin + c * C;
+        store_vt<TPR>(sVT, cg, r, R.v);
+        if (c > 0) load_one<TPR>(R.v, rs.v, t0 - C, r, cg);
+        float l2a[TPR][8], l2b[TPR][8], lend[8];
+        gates_scan<C, false>(R, t0, p.T, r, l, l2a, l2b, lend);
+        if (c > 0) {
+            load_one<TPR>(R.g, rs.g, t0 - C, r, cg);
+            load_one<TPR>(R.th, rs.th, t0 - C, r, cg);
+        }
+        float kbT[8][TPR];
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) {
+            float kf[8];
+            unpack8(R.k[tt], kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kbT[e][tt] = kf[e] * exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e] + rho[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rho[e] += lend[e];
+        if (c > 0) load_one<TPR>(R.k, rs.k, t0 - C, r, cg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_t_rows<TPR>(sKbT, 8 * cg + e, r, kbT[e]);
+        __syncthreads();
+        bf16x8_t vB[C / 16];
+#pragma unroll
+        for (int s = 0; s < C / 16; ++s) vB[s] = lds16(sVT, ((32 * w + l32) * kTRow + 16 * s + 8 * h) * 2);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int s = 0; s < C / 16; ++s)
+                S[mt] = mfma(lds16(sKbT, ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
+        __syncthreads();
+    }
+    float *So = p.wsS + ((size_t)sub * p.BH + bh) * kD * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) So[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * w + l32] = S[mt][i];
+    if (r == 0) {
+        float *A = p.wsA + ((size_t)sub * p.BH + bh) * kD + 8 * cg;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) A[e] = rho[e];
+    }
+}
+
+// Phase 2: run the sub-segment states left to right,
+//   S <- diag(2^{A_j}) S + S_loc[j],
+// storing S into the slot of the last sub-segment of every segment (the
+// incoming state of the next segment).  One thread per (b,h, state element).
 __global__ __launch_bounds__(256)
 void scan_combine_kernel(const float *__restrict__ S0, float *wsS, const float *__restrict__ wsA,
-                         int BH, int nseg) {
+                         int BH, int nsub, int P) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t per = (size_t)kD * kD;
     if (idx >= (size_t)BH * per) return;
-    const size_t bh = idx / per, e = idx % per;
-    const int i = (int)(e / kD);
+    const size_t bh = idx / per;
+    const int i = (int)((idx % per) / kD);
     float s = S0 ? S0[idx] : 0.f;
-    for (int j = 0; j < nseg; ++j) {
-        const size_t base = (size_t)j * BH * per;
-        s = exp2_fast(wsA[((size_t)j * BH + bh) * kD + i]) * s + wsS[base + idx];
-        wsS[base + idx] = s;
+    for (int j = 0; j < nsub; ++j) {
+        const size_t slot = (size_t)j * BH * per + idx;
+        s = exp2_fast(wsA[((size_t)j * BH + bh) * kD + i]) * s + wsS[slot];
+        if ((j + 1) % P == 0) wsS[slot] = s;
     }
+}
+
+struct Plan3 {
+    int G, per_seg, P, sub;  // segments, chunks per segment, sub-segments, chunks per sub-segment
+};
+
+Plan3 plan3(long long BH, long long nchunks) {
+    Plan3 q{1, (int)nchunks, 1, (int)nchunks};
+    long long G = (kCUs + BH - 1) / BH;  // phase 3: one 8-wave workgroup per CU
+    if (G > nchunks) G = nchunks;
+    if (G < 1) G = 1;
+    const long long per_seg = (nchunks + G - 1) / G;
+    G = (nchunks + per_seg - 1) / per_seg;
+    q.G = (int)G;
+    q.per_seg = (int)per_seg;
+    if (G > 1) {
+        long long P = (2 * kCUs + (G - 1) * BH - 1) / ((G - 1) * BH);  // phase 1: ~2 per CU
+        if (P > per_seg) P = per_seg;
+        const long long sub = (per_seg + P - 1) / P;
+        q.P = (int)((per_seg + sub - 1) / sub);
+        q.sub = (int)sub;
+    }
+    return q;
 }
 
 }  // namespace
 
 ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     ScanPlan pl{false, 1, 0};
-    if (!(dtype == 1 && dk == kD && dv == kD && (chunk == 32 || chunk == 64))) return pl;
+    if (!(dtype == 1 && dk == kD && dv == kD && (chunk == 32 || chunk == 64) && T < kMaxT)) return pl;
     pl.mfma = true;
     const long long BH = (long long)B * H;
     const long long nchunks = (T + chunk - 1) / chunk;
-    if (nchunks == 0 || BH == 0) return pl;  // nothing to scan: one segment, no workspace
-    long long G = (kTargetBlocks + BH - 1) / BH;
-    if (G > nchunks) G = nchunks;
-    if (G < 1) G = 1;
-    const long long per_seg = (nchunks + G - 1) / G;  // chunks per segment
-    G = (nchunks + per_seg - 1) / per_seg;
-    pl.segments = (int)G;
-    pl.workspace_bytes = (size_t)(G - 1) * BH * (kD * kD + kD) * sizeof(float);
+    if (nchunks == 0 || BH == 0) return pl;
+    const Plan3 q = plan3(BH, nchunks);
+    pl.segments = q.G;
+    if (q.G > 1) pl.workspace_bytes = (size_t)(q.G - 1) * q.P * BH * (kD * kD + kD) * sizeof(float);
     return pl;
 }
 
 void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
+    (void)pl;
     const int BH = a.B * a.H;
-    const int G = pl.segments;
     const int nchunks = (a.T + a.chunk - 1) / a.chunk;
-    const int per_seg = (nchunks + G - 1) / G;
+    const Plan3 q = plan3(BH, nchunks);
     Params p;
     p.q = (const bf16_t *)a.q; p.k = (const bf16_t *)a.k; p.v = (const bf16_t *)a.v;
     p.g = (const bf16_t *)a.g; p.th = (const bf16_t *)a.tau;
     p.S0 = a.S0; p.o = (bf16_t *)a.o; p.S_T = a.S_T;
+    const int nsub = (q.G - 1) * q.P;
     p.wsS = (float *)a.workspace;
-    p.wsA = p.wsS ? p.wsS + (size_t)(G > 1 ? G - 1 : 0) * BH * kD * kD : nullptr;
-    p.BH = BH; p.T = a.T; p.G = G; p.seg_len = per_seg * a.chunk;
-    if (G > 1) {
-        if (a.chunk == 64) hipLaunchKernelGGL((scan_mfma_kernel<64, false>), dim3((G - 1) * BH), dim3(kThreads), 0, st, p);
-        else hipLaunchKernelGGL((scan_mfma_kernel<32, false>), dim3((G - 1) * BH), dim3(kThreads), 0, st, p);
+    p.wsA = p.wsS ? p.wsS + (size_t)nsub * BH * kD * kD : nullptr;
+    p.BH = BH; p.T = a.T; p.G = q.G; p.seg_len = q.per_seg * a.chunk; p.P = q.P;
+    p.sub_len = q.sub * a.chunk;
+    if (q.G > 1) {
+        if (a.chunk == 64) hipLaunchKernelGGL((scan_state_kernel<64>), dim3(nsub * BH), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((scan_state_kernel<32>), dim3(nsub * BH), dim3(256), 0, st, p);
         const size_t n = (size_t)BH * kD * kD;
         hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                           a.S0, p.wsS, p.wsA, BH, G - 1);
+                           a.S0, p.wsS, p.wsA, BH, nsub, q.P);
     }
-    if (a.chunk == 64) hipLaunchKernelGGL((scan_mfma_kernel<64, true>), dim3(G * BH), dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((scan_mfma_kernel<32, true>), dim3(G * BH), dim3(kThreads), 0, st, p);
+    if (a.chunk == 64) hipLaunchKernelGGL((scan_full_kernel<64>), dim3(q.G * BH), dim3(512), 0, st, p);
+    else hipLaunchKernelGGL((scan_full_kernel<32>), dim3(q.G * BH), dim3(512), 0, st, p);
 }
 
 }  // namespace rodimus
