@@ -34,9 +34,10 @@
 // from the other LDS buffer; one barrier per chunk.  Each consumer wave owns 32
 // of the 128 state columns: its fp32 128x32 state slice lives in MFMA
 // accumulator registers for the whole segment.  The masked score tiles stay in
-// registers too: A^T = Kh Qt^T is built in accumulator layout, which is already
-// the operand layout of o^T += V^T A^T under a permuted k order.  o is produced
-// transposed (o^T = S^T Qt^T + V^T A^T) so that each lane stores 8-byte runs.
+// The masked score tiles A^T = Kh Qt^T are built once per chunk (one tile per
+// consumer wave) and exchanged through LDS behind a barrier of the four
+// consumer waves only.  o is produced transposed (o^T = S^T Qt^T + V^T A^T) so
+// that each lane stores 8-byte runs.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operand A[m][k] sits in lane m + 32*(k/8),
 // element k%8; B[k][n] in lane n + 32*(k/8), element k%8; the accumulator
@@ -67,6 +68,8 @@ constexpr int kOffKbT = kOffK + 64 * kQRow * 2;
 constexpr int kOffVT = kOffKbT + kD * kTRow * 2;
 constexpr int kOffGam = kOffVT + kD * kTRow * 2;
 constexpr int kBufBytes = kOffGam + kD * 4;
+constexpr int kARow = 64 + 8;      // bf16 per row of sA [C][C] (token i, token j permuted)
+constexpr int kSABytes = 64 * kARow * 2;
 
 struct Params {
     const bf16_t *q, *k, *v, *g, *th;
@@ -250,8 +253,10 @@ template <int C>
 __global__ __launch_bounds__(512, 1)
 void scan_full_kernel(Params p) {
     constexpr int TPR = C / 16, NT = C / 32;
-    __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + 16];
-    int *sFlag = reinterpret_cast<int *>(smem + 2 * kBufBytes);  // chunk k -> slot k % 3
+    __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + kSABytes + 16];
+    char *sA = smem + 2 * kBufBytes;                                        // score tiles of one chunk
+    int *sFlag = reinterpret_cast<int *>(smem + 2 * kBufBytes + kSABytes);  // chunk k -> slot k % 3
+    int *sCBar = sFlag + 3;                                                 // consumer-wave barrier
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
     const int bh = uni(blockIdx.x % p.BH), seg = uni(blockIdx.x / p.BH);
@@ -261,7 +266,7 @@ void scan_full_kernel(Params p) {
     const int nch = (t_end - t_begin + C - 1) / C;
     const size_t rowbase = (size_t)bh * p.T;
 
-    if (tid < 3) sFlag[tid] = 0;
+    if (tid < 4) sFlag[tid] = 0;
     __syncthreads();
 
     if (w < 4) {
@@ -329,7 +334,11 @@ void scan_full_kernel(Params p) {
     }
 
     // ======================= consumers =======================
+    // The consumer waves' MFMA chain is the shorter critical path of an interval:
+    // issue it first and let the producer waves fill the VALU around it.
+    __builtin_amdgcn_s_setprio(3);
     const int cw = w - 4;                 // state columns 32cw .. 32cw+31
+    int cbar_target = 0;
     const int n = 32 * cw + l32;
     f32x16_t S[4];                        // rows 32mt + 8a + 4h + r4, column n
     {
@@ -404,25 +413,41 @@ void scan_full_kernel(Params p) {
                 bf16x8_t Sb[8];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) Sb[s] = cvt8(S[s >> 1], 8 * (s & 1));
-                // masked score tiles A^T[j][i] = Kh[j] . Qt[i] (j <= i), accumulator layout;
-                // (Jt, It) = (0,0), (0,1), (1,1), only the first for C = 32
-                f32x16_t At[NT == 2 ? 3 : 1];
-#pragma unroll
-                for (int ti = 0; ti < (NT == 2 ? 3 : 1); ++ti) {
-                    const int Jt = (ti == 2) ? 1 : 0, It = (ti == 0) ? 0 : 1;
-                    At[ti] = f32x16_t{};
+                // masked score tiles A^T[j][i] = Kh[j] . Qt[i] (j <= i); consumer wave ti
+                // builds tile (Jt, It) = (0,0), (0,1), (1,1) (only (0,0) for C = 32) and
+                // stores it as A[i][j] (j in permuted order) for all four waves
+                if (cw < (NT == 2 ? 3 : 1)) {
+                    const int Jt = (cw == 2) ? 1 : 0, It = (cw == 0) ? 0 : 1;
+                    f32x16_t at = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
                         const bf16x8_t a = lds16(buf, kOffK + ((32 * Jt + l32) * kQRow + 16 * s + 8 * h) * 2);
                         const bf16x8_t b = lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2);
-                        At[ti] = mfma(a, b, At[ti]);
+                        at = mfma(a, b, at);
                     }
-                    if (Jt == It) {
+                    const int i = 32 * It + l32;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (8 * (i >> 2) + 4 * h + (i & 3) > l32) At[ti][i] = 0.f;
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        float x[4];
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) {
+                            const int j = 32 * Jt + 8 * a4 + 4 * h + r4;
+                            x[r4] = (j <= i) ? at[4 * a4 + r4] : 0.f;
+                        }
+                        *reinterpret_cast<uint2 *>(sA + (i * kARow + perm16(32 * Jt + 8 * a4 + 4 * h)) * 2) =
+                            make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
                     }
                 }
+                // the four consumer waves meet (LDS counter; the producer waves are
+                // not involved); bounded wait
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                if (l == 0) __hip_atomic_fetch_add(sCBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                cbar_target += 4;
+                for (int spin = 0; spin < (1 << 24); ++spin) {
+                    if (__hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= cbar_target) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
                 // o^T tiles: 32 value channels (this wave's) x 32 tokens (32It..).  Same
                 // fragments as o = Qt S + A V with the operands swapped, so that a
                 // lane holds one token and 4 consecutive channels per register group.
@@ -433,10 +458,8 @@ void scan_full_kernel(Params p) {
                     for (int s = 0; s < 8; ++s)
                         acc = mfma(Sb[s], lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2), acc);
 #pragma unroll
-                    for (int s = 0; s < 2 * It + 2; ++s) {
-                        const int ti = (It == 0) ? 0 : (s < 2 ? 1 : 2);
-                        acc = mfma(vB[s], cvt8(At[ti], 8 * (s & 1)), acc);
-                    }
+                    for (int s = 0; s < 2 * It + 2; ++s)
+                        acc = mfma(vB[s], lds16(sA, ((32 * It + l32) * kARow + 16 * s + 8 * h) * 2), acc);
                     const int t = t0 + 32 * It + l32;
                     if (t < t_end) {
                         bf16_t *op = p.o + (rowbase + t) * kD + 32 * cw + 4 * h;
