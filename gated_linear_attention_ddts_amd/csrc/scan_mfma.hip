@@ -581,20 +581,40 @@ void scan_state_kernel(Params p) {
 // Phase 2: run the sub-segment states left to right,
 //   S <- diag(2^{A_j}) S + S_loc[j],
 // storing S into the slot of the last sub-segment of every segment (the
-// incoming state of the next segment).  One thread per (b,h, state element).
+// incoming state of the next segment).  One thread per (b,h, 4 consecutive
+// state elements of one row); all loads of a thread are independent and issued
+// up front.
 __global__ __launch_bounds__(256)
 void scan_combine_kernel(const float *__restrict__ S0, float *wsS, const float *__restrict__ wsA,
                          int BH, int nsub, int P) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t per = (size_t)kD * kD;
-    if (idx >= (size_t)BH * per) return;
-    const size_t bh = idx / per;
-    const int i = (int)((idx % per) / kD);
-    float s = S0 ? S0[idx] : 0.f;
-    for (int j = 0; j < nsub; ++j) {
-        const size_t slot = (size_t)j * BH * per + idx;
-        s = exp2_fast(wsA[((size_t)j * BH + bh) * kD + i]) * s + wsS[slot];
-        if ((j + 1) % P == 0) wsS[slot] = s;
+    const size_t idx4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+    const size_t per4 = (size_t)kD * kD / 4;
+    if (idx4 >= (size_t)BH * per4) return;
+    const size_t bh = idx4 / per4;
+    const int i = (int)((idx4 % per4) / (kD / 4));
+    float4 s = S0 ? reinterpret_cast<const float4 *>(S0)[idx4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int kBatch = 8;
+    for (int j0 = 0; j0 < nsub; j0 += kBatch) {
+        float4 x[kBatch];
+        float a[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = j0 + u;
+            if (j < nsub) {
+                x[u] = reinterpret_cast<const float4 *>(wsS)[(size_t)j * BH * per4 + idx4];
+                a[u] = wsA[((size_t)j * BH + bh) * kD + i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = j0 + u;
+            if (j < nsub) {
+                const float d = exp2_fast(a[u]);
+                s.x = fmaf(d, s.x, x[u].x); s.y = fmaf(d, s.y, x[u].y);
+                s.z = fmaf(d, s.z, x[u].z); s.w = fmaf(d, s.w, x[u].w);
+                if ((j + 1) % P == 0) reinterpret_cast<float4 *>(wsS)[(size_t)j * BH * per4 + idx4] = s;
+            }
+        }
     }
 }
 
@@ -653,8 +673,8 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     if (q.G > 1) {
         if (a.chunk == 64) hipLaunchKernelGGL((scan_state_kernel<64>), dim3(nsub * BH), dim3(256), 0, st, p);
         else hipLaunchKernelGGL((scan_state_kernel<32>), dim3(nsub * BH), dim3(256), 0, st, p);
-        const size_t n = (size_t)BH * kD * kD;
-        hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+        const size_t n4 = (size_t)BH * kD * kD / 4;
+        hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                            a.S0, p.wsS, p.wsA, BH, nsub, q.P);
     }
     if (a.chunk == 64) hipLaunchKernelGGL((scan_full_kernel<64>), dim3(q.G * BH), dim3(512), 0, st, p);

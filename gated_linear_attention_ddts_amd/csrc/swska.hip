@@ -18,7 +18,8 @@
 //                     rescaled only when a lane's running max grows by more than
 //                     2^8 (exact: the final division uses the same reference);
 //   O^T += V^T P^T    P^T taken straight from the S^T accumulators (bf16) with a
-//                     permuted k order; V^T is read from LDS with the same order.
+//                     permuted k order; V^T is stored in LDS in that key order,
+//                     so each operand is one 16-byte read.
 // Tiles entirely outside a wave's window are skipped; tiles on the window's two
 // edges are masked element by element.  Workgroups are mapped so that each XCD
 // works on a fixed pair of heads in increasing query order, which keeps the
@@ -46,6 +47,30 @@ __device__ __forceinline__ f32x16_t mfma(const bf16x8_t &a, const bf16x8_t &b, c
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Position of key index x inside V^T rows: blocks of 4 keys placed 0,2,1,3 in
+// each 16, the k order in which the S^T accumulators hold the keys.
+__device__ __forceinline__ int perm16(int x) {
+    const int blk = (x >> 2) & 3;
+    return (x & ~15) | (((blk & 1) << 1 | (blk >> 1)) << 2) | (x & 3);
+}
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const bf16_t *uni_ptr(const bf16_t *p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<const bf16_t *>(((uint64_t)hi << 32) | lo);
+}
+// Buffer descriptor over rows [0, T) of a [T][D] bf16 matrix; reads past the
+// end return zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16_t *base, int T) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)uni_ptr(base), (short)0, uni(T * D * 2), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 template <int D>
 struct Tile {
     static constexpr int KROW = D + 8;        // bf16 per K row in LDS
@@ -58,25 +83,18 @@ struct Tile {
 };
 
 template <int D>
-__device__ __forceinline__ void fetch_tile(const bf16_t *__restrict__ kb, const bf16_t *__restrict__ vb,
-                                           int k0, int T, uint4 (&rk)[Tile<D>::KVEC],
-                                           uint4 (&rv)[Tile<D>::KPT]) {
+__device__ __forceinline__ void fetch_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int k0,
+                                           uint4 (&rk)[Tile<D>::KVEC], uint4 (&rv)[Tile<D>::KPT]) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < Tile<D>::KVEC; ++i) {
         const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
-        const int key = k0 + row;
-        rk[i] = key < T ? *reinterpret_cast<const uint4 *>(kb + (size_t)key * D + 8 * col)
-                        : make_uint4(0, 0, 0, 0);
+        rk[i] = bload(kr, (k0 + row) * D * 2 + 16 * col);
     }
     constexpr int KPT = Tile<D>::KPT;
     const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int key = k0 + KPT * kg + i;
-        rv[i] = key < T ? *reinterpret_cast<const uint4 *>(vb + (size_t)key * D + 8 * dg)
-                        : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < KPT; ++i) rv[i] = bload(vr, (k0 + KPT * kg + i) * D * 2 + 16 * dg);
 }
 
 template <int D>
@@ -100,7 +118,7 @@ __device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D>:
             const uint32_t word = (e < 2) ? rv[i].x : (e < 4) ? rv[i].y : (e < 6) ? rv[i].z : rv[i].w;
             w[i] = (e & 1) ? (word >> 16) : (word & 0xffffu);
         }
-        const int off = ((8 * dg + e) * Tile<D>::VROW + KPT * kg) * 2;
+        const int off = ((8 * dg + e) * Tile<D>::VROW + perm16(KPT * kg)) * 2;
         if (KPT == 4) {
             *reinterpret_cast<uint2 *>(vt + off) =
                 make_uint2(w[0] | (w[1 % KPT] << 16), w[2 % KPT] | (w[3 % KPT] << 16));
@@ -130,6 +148,8 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         bh = id % BH;
         qb = id / BH;
     }
+    bh = uni(bh);
+    qb = uni(qb);
     if (qb >= nqb) return;
     const int b = bh / H;
 
@@ -137,8 +157,8 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int q0 = qb * kBQ;
     const int qw0 = q0 + 32 * w;            // this wave's first query
     const int qi = qw0 + l32;               // this lane's query
-    const bf16_t *kb = k + (size_t)b * T * D;
-    const bf16_t *vb = v + (size_t)bh * T * D;
+    const __amdgpu_buffer_rsrc_t kr = rsrc<D>(k + (size_t)b * T * D, T);
+    const __amdgpu_buffer_rsrc_t vr = rsrc<D>(v + (size_t)bh * T * D, T);
 
     // Q^T operand fragments (B operand: n = query, k = channel)
     bf16x8_t qB[D / 16];
@@ -161,31 +181,29 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int wlo = qw0 - window + 1, whi = qw0 + 31;
 
     uint4 rk[TL::KVEC], rv[TL::KPT];
-    fetch_tile<D>(kb, vb, kt0, T, rk, rv);
+    fetch_tile<D>(kr, vr, kt0, rk, rv);
     store_tile<D>(smem, rk, rv);
     __syncthreads();
 
     int buf = 0;
     for (int k0 = kt0; k0 < hi; k0 += kBK, buf ^= 1) {
         const bool more = k0 + kBK < hi;
-        if (more) fetch_tile<D>(kb, vb, k0 + kBK, T, rk, rv);
+        if (more) fetch_tile<D>(kr, vr, k0 + kBK, rk, rv);
         const char *cur = smem + buf * TL::BYTES;
 
         const bool skip = (k0 + kBK - 1 < wlo) || (k0 > whi);
         if (!skip) {
             const bool edge = (k0 <= whi - window) || (k0 + kBK - 1 > qw0) || (k0 + kBK > T);
             // S^T tile: 64 keys x 32 queries
-            f32x16_t S[2];
+            f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                S[mt] = f32x16_t{};
+            for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
+                for (int mt = 0; mt < 2; ++mt) {
                     const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
                         cur + ((32 * mt + l32) * TL::KROW + 16 * s + 8 * h) * 2);
                     S[mt] = mfma(a, qB[s], S[mt]);
                 }
-            }
             if (edge) {
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
@@ -230,13 +248,12 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             // O^T += V^T P^T: k = key in the permuted order of the S^T accumulators
             const char *vt = cur + TL::KBYTES;
 #pragma unroll
-            for (int mt = 0; mt < D / 32; ++mt)
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int off = ((32 * mt + l32) * TL::VROW + 16 * s + 4 * h) * 2;
-                    bf16x4_t a0 = *reinterpret_cast<const bf16x4_t *>(vt + off);
-                    bf16x4_t a1 = *reinterpret_cast<const bf16x4_t *>(vt + off + 16);
-                    O[mt] = mfma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), P[s], O[mt]);
+                for (int mt = 0; mt < D / 32; ++mt) {
+                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                        vt + ((32 * mt + l32) * TL::VROW + 16 * s + 8 * h) * 2);
+                    O[mt] = mfma(a, P[s], O[mt]);
                 }
         }
         if (more) store_tile<D>(smem + (buf ^ 1) * TL::BYTES, rk, rv);
