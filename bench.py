@@ -1,28 +1,41 @@
 """Benchmark of the Rodimus* token-mixer hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-extras]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+                    [--only all|prefill|decode|long|swska|copy]
 
 A step is one rodimus_scan_prefill call over the 1.6B-shaped prefill batch
 (B=4, T=4096, H=16, dk=dv=128, bf16 inputs, fp32 state, C=64) with every input
-already resident in HBM.  value = B*T / step time (prefill tokens/s).  The
-decode state update (256 sequences x 16 heads, fp32 128x128 states, 1000
-in-place steps cycling over 8 resident input sets) is timed in the same run and
-reported as HBM GB/s and fraction of peak, as the metric asks.  The long-context
-prefill (T=131072) and SW-SKA (T=32768, w=4096) are timed as extras.
+already resident in HBM; value = B*T / step time (prefill tokens/s).  The
+decode state update (256 sequences x 16 heads, fp32 128x128 states, in-place
+steps cycling over 8 resident input sets) is timed in the same run and
+reported as HBM GB/s and fraction of peak, as the metric asks.  The
+long-context prefill (T=131072) and SW-SKA (T=32768, w=4096) are timed as
+extras.
 
 Timing: W untimed warm-up steps, then K steps between two HIP events on the
 stream the kernels run on (torch's current stream), with device syncs on both
-sides.  Algorithmic bytes per token-head of the prefill: q, k, g, tau (4 x 256 B)
-+ v (256 B) in, o (256 B) out = 1536 B, plus the fp32 final state.  Decode:
-the fp32 state read and written (2 x 64 KiB per head) plus 5 x 256 B inputs and
-256 B output per head.  Peaks: HBM 8 TB/s; dense bf16 MFMA 2.5 PFLOP/s.
+sides.  One prefill call launches up to three kernels (segment states, their
+combination, the output pass); the roofline entry is for that whole call.
 
-The CPU baseline is the fp64 oracle run on the host cores over a bounded sample
-of the same workload (stated in the "sample" field).
+Algorithmic bytes: prefill, per token-head, q, k, g, tau (4 x 256 B) + v (256 B)
+in and o (256 B) out = 1536 B, plus the fp32 final state; decode, per head, the
+fp32 state read and written (2 x 64 KiB) plus 5 x 256 B of inputs and 256 B of
+output; SW-SKA, q, v, o per token-head and the shared k per token.  Peaks: HBM
+8 TB/s; dense bf16 MFMA 2.5 PFLOP/s.
+
+"traffic" is the HBM byte count per call measured with rocprofv3 counters
+(FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), read from
+profiles/traffic.json when that file was taken from the current kernel sources
+(same source hash); otherwise null.
+
+The CPU baseline is the fp64 oracle run on the host cores over the whole
+prefill workload (the "sample" field says so).  --only selects one workload and
+skips the JSON summary line (used under rocprofv3).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +51,33 @@ METRIC = "prefill tokens/s (H16,d128,T4K) + decode state-update HBM GB/s, % roof
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 NAMES = ("q", "k", "v", "g", "theta")
+CSRC = os.path.join(ROOT, "gated_linear_attention_ddts_amd", "csrc")
+KERNEL_SOURCES = {
+    "prefill": ("scan_mfma.hip", "device_common.h"),
+    "decode": ("decode.hip", "device_common.h"),
+    "swska": ("swska.hip", "device_common.h"),
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per call from profiles/traffic.json, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kind):
+        return None
+    return rec.get("bytes_per_call")
 
 
 def _dev(t):
@@ -98,6 +138,10 @@ def bench_prefill(cfg, steps, warmup):
                 workspace_bytes=nws)
 
 
+def decode_bytes(N, H, dk, dv):
+    return N * H * (2 * dk * dv * 4 + (4 * dk + dv) * 2 + dv * 2)
+
+
 def bench_decode(cfg, steps, warmup):
     import torch
     import gated_linear_attention_ddts_amd as rd
@@ -115,9 +159,15 @@ def bench_decode(cfg, steps, warmup):
         rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], S, o=o)
 
     ms = _time(step, steps, warmup)
-    nbytes = N * H * (2 * dk * dv * 4 + (3 * dk + dv + dk) * 2 + dv * 2)
+    nbytes = decode_bytes(N, H, dk, dv)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
                 gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+
+
+def swska_pairs(T, w):
+    # query-key pairs inside the causal band: sum_t min(t+1, w)
+    n = min(T, w)
+    return n * (n + 1) // 2 + (T - n) * w
 
 
 def bench_swska(cfg, steps, warmup):
@@ -128,45 +178,44 @@ def bench_swska(cfg, steps, warmup):
     x = workloads.swska_inputs(cfg["seed"], B, H, T, dk, dv)
     d = {n: _dev(x[n]) for n in ("q", "k", "v")}
     o = torch.empty(B, H, T, dv, dtype=torch.bfloat16, device="cuda")
-    try:
-        rd.sw_ska_attn(d["q"], d["k"], d["v"], w, o=o)
-    except rd.RodimusError as ex:
-        return dict(status=str(ex))
 
     def step():
         rd.sw_ska_attn(d["q"], d["k"], d["v"], w, o=o)
 
     ms = _time(step, steps, warmup)
-    # query-key pairs inside the window (causal band), 4*d flops each
-    pairs = 0
-    for t in range(T):
-        pairs += min(t + 1, w)
-    pairs *= B * H
-    flops = pairs * 2 * (dk + dv)
+    flops = B * H * swska_pairs(T, w) * 2 * (dk + dv)
     nbytes = (B * H * T * (dk + 2 * dv) + B * T * dk) * 2
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), flops=flops,
                 tflops=flops / (ms * 1e-3) / 1e12, bytes=nbytes)
 
 
+def bench_copy(nbytes=1 << 30, steps=5):
+    """A plain device-to-device copy of known size (counter calibration)."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    ms = _time(lambda: b.copy_(a), steps, 1)
+    return dict(ms=ms, read_bytes=a.numel(), write_bytes=b.numel(),
+                gbs=2 * a.numel() / (ms * 1e-3) / 1e9)
+
+
 def cpu_baseline(cfg):
-    """The fp64 oracle on the host cores over a bounded sample of the prefill
-    workload: the first `heads` (b, h) pairs, full sequence length."""
+    """The fp64 oracle on the host cores over the whole prefill workload."""
     import oracle
     import workloads
     cores = min(os.cpu_count() or 1, 16)
-    heads = min(cfg["B"] * cfg["H"], max(cores, 16))
     x = workloads.scan_inputs(cfg["seed"], cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"],
                               cfg["dtype"], gate_mu=cfg["gate_mu"])
-    BH = cfg["B"] * cfg["H"]
-    flat = {n: x[n].values.reshape(1, BH, cfg["T"], -1)[:, :heads].astype(np.float64) for n in NAMES}
+    arrs = [x[n].f64() for n in NAMES]
+    del x
     t0 = time.perf_counter()
-    oracle.scan(*(flat[n] for n in NAMES), nthreads=cores)
+    oracle.scan(*arrs, nthreads=cores)
     dt = time.perf_counter() - t0
-    # tokens/s of the whole B x T batch at this rate (every (b,h) costs the same)
-    token_heads_per_s = heads * cfg["T"] / dt
-    return dict(value=token_heads_per_s / cfg["H"], unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{heads} of {BH} (b,h) pairs x T={cfg['T']} (fp64 sequential scan, "
-                       f"{dt:.2f} s); rate scaled to B*T tokens over H={cfg['H']} heads")
+    BT = cfg["B"] * cfg["T"]
+    return dict(value=round(BT / dt, 1), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"the whole workload: B={cfg['B']} x T={cfg['T']} tokens x H={cfg['H']} "
+                       f"heads, fp64 sequential scan per (b,h) on {cores} threads, {dt:.2f} s wall")
 
 
 def main():
@@ -176,12 +225,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(every (b,h) pair and segment is independent per GPU; see the sharding notes).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
+              "sequence and head is independent, so N GPUs would each run this same workload on "
+              "their own share (weak scaling).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -189,36 +238,39 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.only != "all":
+        if args.only == "prefill":
+            r = bench_prefill(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup)
+        elif args.only == "long":
+            r = bench_prefill(workloads.CONFIGS["prefill_long_T131072"], args.steps, args.warmup)
+        elif args.only == "decode":
+            r = bench_decode(workloads.CONFIGS["decode_N256"], args.steps, args.warmup)
+        elif args.only == "swska":
+            r = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], args.steps, args.warmup)
+        else:
+            r = bench_copy()
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
+              flush=True)
+        return
+
     cfg = workloads.CONFIGS["prefill_1p6b_T4096"]
     print("bench: prefill_1p6b_T4096", file=sys.stderr, flush=True)
     pre = bench_prefill(cfg, args.steps, args.warmup)
     print("bench: decode_N256", file=sys.stderr, flush=True)
     dec = bench_decode(workloads.CONFIGS["decode_N256"], args.decode_steps, 10)
-
-    extras = {}
-    if not args.no_extras:
-        print("bench: prefill_long_T131072", file=sys.stderr, flush=True)
-        lc = workloads.CONFIGS["prefill_long_T131072"]
-        r = bench_prefill(lc, max(3, args.steps // 4), 1)
-        extras["prefill_long_T131072"] = dict(
-            ms=round(r["ms"], 4), tokens_per_s=round(r["tokens_per_s"]),
-            gbs=round(r["gbs"], 1), frac_hbm=round(r["gbs"] / HBM_PEAK_GBS, 4),
-            mfma_frac=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
-        print("bench: swska_T32768_w4096", file=sys.stderr, flush=True)
-        sc = workloads.CONFIGS["swska_T32768_w4096"]
-        r = bench_swska(sc, max(3, args.steps // 4), 1)
-        if "ms" in r:
-            r = dict(ms=round(r["ms"], 4), tokens_per_s=round(r["tokens_per_s"]),
-                     tflops=round(r["tflops"], 1),
-                     frac_mfma=round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4))
-        extras["swska_T32768_w4096"] = r
+    print("bench: prefill_long_T131072", file=sys.stderr, flush=True)
+    lc = workloads.CONFIGS["prefill_long_T131072"]
+    lr = bench_prefill(lc, max(3, args.steps // 4), 1)
+    print("bench: swska_T32768_w4096", file=sys.stderr, flush=True)
+    sr = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], max(3, args.steps // 4), 1)
 
     cpu = None
     if not args.no_cpu:
-        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg)
-        cpu["value"] = round(cpu["value"], 1)
 
+    tr = measured_traffic("prefill_1p6b_T4096", "prefill")
+    dtr = measured_traffic("decode_N256", "decode")
     line = {
         "metric": METRIC,
         "value": round(pre["tokens_per_s"], 1),
@@ -237,13 +289,28 @@ def main():
                    "state_dtype": "fp32"},
         "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "rodimus_scan_prefill (one call)",
+                     "traffic": tr, "kernel": "rodimus_scan_prefill call (segment states + "
+                     "combine + output pass)", "algorithmic_bytes": pre["bytes"],
                      "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "decode": {"workload": "decode_N256", "us_per_step": round(dec["us_per_step"], 2),
-                   "tokens_per_s": round(dec["tokens_per_s"]), "gbs": round(dec["gbs"], 1),
-                   "frac_hbm": round(dec["gbs"] / HBM_PEAK_GBS, 4), "steps": dec["steps"]},
-        "extras": extras,
+                   "tokens_per_s": round(dec["tokens_per_s"]), "steps": dec["steps"],
+                   "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": dtr,
+                                "kernel": "decode_step_kernel<bf16,128,128>",
+                                "algorithmic_bytes": dec["bytes"]}},
+        "extras": {
+            "prefill_long_T131072": {
+                "ms": round(lr["ms"], 4), "tokens_per_s": round(lr["tokens_per_s"]),
+                "roofline": {"bound": "hbm", "achieved": round(lr["gbs"], 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(lr["gbs"] / HBM_PEAK_GBS, 4)}},
+            "swska_T32768_w4096": {
+                "ms": round(sr["ms"], 4), "tokens_per_s": round(sr["tokens_per_s"]),
+                "roofline": {"bound": "mfma", "achieved": round(sr["tflops"], 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}},
+        },
     }
     print(json.dumps(line), flush=True)
 

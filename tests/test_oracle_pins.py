@@ -344,3 +344,23 @@ def test_swska_row_subset():
     flat_p = part.reshape(-1, dv)
     assert np.array_equal(flat_p[rows], flat_f[rows])
     assert np.isnan(flat_p[1]).all()
+
+
+# ------------------------------------------------------------------ golden
+
+def test_golden_fixture_reproduced():
+    """Regression lock: tests/golden/oracle_tiny.json (written by
+    tests/golden/make_golden.py from the oracle) is reproduced exactly."""
+    import json
+    import os
+    rec = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "oracle_tiny.json")))
+    a = {k: np.array(rec[k]) for k in ("q", "k", "v", "g", "theta", "S0", "o", "S_T")}
+    o, ST = oracle.scan(a["q"], a["k"], a["v"], a["g"], a["theta"], a["S0"])
+    np.testing.assert_allclose(o, a["o"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(ST, a["S_T"], rtol=1e-14, atol=1e-15)
+    la, lb = oracle.gates(a["g"], a["theta"])
+    np.testing.assert_allclose(la, rec["log_a"], rtol=1e-14)
+    np.testing.assert_allclose(lb, rec["log_beta"], rtol=1e-14)
+    os_ = oracle.swska(np.array(rec["swska_q"]), np.array(rec["swska_k"]), np.array(rec["swska_v"]),
+                       rec["swska_window"])
+    np.testing.assert_allclose(os_, rec["swska_o"], rtol=1e-14, atol=1e-15)
