@@ -21,7 +21,8 @@
 // sequence of each (b, h) is cut into G segments (each a whole number of
 // chunks), and every segment but the last into P sub-segments:
 //   phase 1 (scan_state_kernel): each sub-segment's local end state (from zero)
-//            and its total log2 decay.  Chunks are visited last to first, so the
+//            and its total log2 decay, in 32-token chunks with two chunks of
+//            inputs in flight.  Chunks are visited last to first, so the
 //            decay of the later chunks folds into the operand exponent:
 //            S_loc = sum_c (Kb_c * 2^{rho_c})^T V_c, rho_c = sum of Lam_end after c;
 //            there is no state rescaling and nothing can overflow;
@@ -498,10 +499,50 @@ void scan_full_kernel(Params p) {
 }
 
 // ----------------------------------------------------------- phase 1 (state)
-template <int C>
+// One sub-segment's local end state.  Processed in chunks of 32 tokens whatever
+// the caller's C (the result does not depend on the chunking), which leaves
+// room in the registers for two chunks of raw inputs in flight.
+template <int TPR>
+__device__ __forceinline__ void state_chunk(Raw<16 * TPR, false> &R, const Rsrc &rs, int t0, int tnext,
+                                            char *sKbT, char *sVT, f32x16_t (&S)[4], float (&rho)[8],
+                                            int r, int cg, int l, int w, int h, int l32, int T) {
+    store_vt<TPR>(sVT, cg, r, R.v);
+    if (tnext >= 0) load_one<TPR>(R.v, rs.v, tnext, r, cg);
+    float l2a[TPR][8], l2b[TPR][8], lend[8];
+    gates_scan<16 * TPR, false>(R, t0, T, r, l, l2a, l2b, lend);
+    if (tnext >= 0) {
+        load_one<TPR>(R.g, rs.g, tnext, r, cg);
+        load_one<TPR>(R.th, rs.th, tnext, r, cg);
+    }
+    float kbT[8][TPR];
+#pragma unroll
+    for (int tt = 0; tt < TPR; ++tt) {
+        float kf[8];
+        unpack8(R.k[tt], kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            kbT[e][tt] = kf[e] * exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e] + rho[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rho[e] += lend[e];
+    if (tnext >= 0) load_one<TPR>(R.k, rs.k, tnext, r, cg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store_t_rows<TPR>(sKbT, 8 * cg + e, r, kbT[e]);
+    __syncthreads();
+    bf16x8_t vB[TPR];
+#pragma unroll
+    for (int s = 0; s < TPR; ++s) vB[s] = lds16(sVT, ((32 * w + l32) * kTRow + 16 * s + 8 * h) * 2);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int s = 0; s < TPR; ++s)
+            S[mt] = mfma(lds16(sKbT, ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(256, 2)
 void scan_state_kernel(Params p) {
-    constexpr int TPR = C / 16;
+    constexpr int CS = 32, TPR = CS / 16;
     __shared__ __attribute__((aligned(16))) char smem[2 * kD * kTRow * 2];
     char *sKbT = smem, *sVT = smem + kD * kTRow * 2;
 
@@ -513,7 +554,7 @@ void scan_state_kernel(Params p) {
     const int seg_begin = seg * p.seg_len;
     const int t_begin = seg_begin + part * p.sub_len;
     const int t_end = min(seg_begin + p.seg_len, t_begin + p.sub_len);  // whole chunks
-    const int nch = (t_end - t_begin) / C;
+    const int nch = (t_end - t_begin) / CS;
     const size_t rowbase = (size_t)bh * p.T;
     const int r = l & 15, cg = (w << 2) | (l >> 4);
 
@@ -529,42 +570,17 @@ void scan_state_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) rho[e] = 0.f;
 
-    Raw<C, false> R;
-    load_raw<C, false>(R, rs, t_begin + (nch - 1) * C, r, cg);
-    for (int c = nch - 1; c >= 0; --c) {
-        const int t0 = t_begin + c * C;
-        store_vt<TPR>(sVT, cg, r, R.v);
-        if (c > 0) load_one<TPR>(R.v, rs.v, t0 - C, r, cg);
-        float l2a[TPR][8], l2b[TPR][8], lend[8];
-        gates_scan<C, false>(R, t0, p.T, r, l, l2a, l2b, lend);
-        if (c > 0) {
-            load_one<TPR>(R.g, rs.g, t0 - C, r, cg);
-            load_one<TPR>(R.th, rs.th, t0 - C, r, cg);
-        }
-        float kbT[8][TPR];
-#pragma unroll
-        for (int tt = 0; tt < TPR; ++tt) {
-            float kf[8];
-            unpack8(R.k[tt], kf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                kbT[e][tt] = kf[e] * exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e] + rho[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rho[e] += lend[e];
-        if (c > 0) load_one<TPR>(R.k, rs.k, t0 - C, r, cg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) store_t_rows<TPR>(sKbT, 8 * cg + e, r, kbT[e]);
-        __syncthreads();
-        bf16x8_t vB[C / 16];
-#pragma unroll
-        for (int s = 0; s < C / 16; ++s) vB[s] = lds16(sVT, ((32 * w + l32) * kTRow + 16 * s + 8 * h) * 2);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int s = 0; s < C / 16; ++s)
-                S[mt] = mfma(lds16(sKbT, ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
-        __syncthreads();
+    // chunks are visited last to first; two chunks of raw inputs are in flight
+    Raw<CS, false> Ra, Rb;
+    const int c0 = nch - 1;
+    load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
+    if (c0 >= 1) load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
+    for (int c = c0; c >= 0; c -= 2) {
+        state_chunk<TPR>(Ra, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1, sKbT, sVT,
+                         S, rho, r, cg, l, w, h, l32, p.T);
+        if (c >= 1)
+            state_chunk<TPR>(Rb, rs, t_begin + (c - 1) * CS, c >= 3 ? t_begin + (c - 3) * CS : -1,
+                             sKbT, sVT, S, rho, r, cg, l, w, h, l32, p.T);
     }
     float *So = p.wsS + ((size_t)sub * p.BH + bh) * kD * kD;
 #pragma unroll
@@ -671,8 +687,7 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.BH = BH; p.T = a.T; p.G = q.G; p.seg_len = q.per_seg * a.chunk; p.P = q.P;
     p.sub_len = q.sub * a.chunk;
     if (q.G > 1) {
-        if (a.chunk == 64) hipLaunchKernelGGL((scan_state_kernel<64>), dim3(nsub * BH), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((scan_state_kernel<32>), dim3(nsub * BH), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(scan_state_kernel, dim3(nsub * BH), dim3(256), 0, st, p);
         const size_t n4 = (size_t)BH * kD * kD / 4;
         hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                            a.S0, p.wsS, p.wsA, BH, nsub, q.P);
