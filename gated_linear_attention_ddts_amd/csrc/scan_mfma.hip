@@ -648,7 +648,10 @@ Plan3 plan3(long long BH, long long nchunks) {
     q.G = (int)G;
     q.per_seg = (int)per_seg;
     if (G > 1) {
-        long long P = (2 * kCUs + (G - 1) * BH - 1) / ((G - 1) * BH);  // phase 1: ~2 per CU
+        // phase 1: ~1.5 workgroups per CU (it is bandwidth-bound; more sub-segments
+        // only add state traffic to the combine)
+        long long P = (3 * kCUs + (G - 1) * BH) / (2 * (G - 1) * BH);
+        if (P < 1) P = 1;
         if (P > per_seg) P = per_seg;
         const long long sub = (per_seg + P - 1) / P;
         q.P = (int)((per_seg + sub - 1) / sub);
