@@ -112,19 +112,20 @@ __device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D>:
     char *vt = buf + Tile<D>::KBYTES;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        uint32_t w[KPT];
+        // element e of keys 2i and 2i+1 -> one word (v_perm: the low or the high
+        // halves of the two source words)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[KPT / 2];
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const uint32_t word = (e < 2) ? rv[i].x : (e < 4) ? rv[i].y : (e < 6) ? rv[i].z : rv[i].w;
-            w[i] = (e & 1) ? (word >> 16) : (word & 0xffffu);
+        for (int i = 0; i < KPT / 2; ++i) {
+            const uint4 &a = rv[2 * i], &c = rv[2 * i + 1];
+            const uint32_t wa = (e < 2) ? a.x : (e < 4) ? a.y : (e < 6) ? a.z : a.w;
+            const uint32_t wc = (e < 2) ? c.x : (e < 4) ? c.y : (e < 6) ? c.z : c.w;
+            w[i] = __builtin_amdgcn_perm(wc, wa, sel);
         }
         const int off = ((8 * dg + e) * Tile<D>::VROW + perm16(KPT * kg)) * 2;
-        if (KPT == 4) {
-            *reinterpret_cast<uint2 *>(vt + off) =
-                make_uint2(w[0] | (w[1 % KPT] << 16), w[2 % KPT] | (w[3 % KPT] << 16));
-        } else {
-            *reinterpret_cast<uint32_t *>(vt + off) = w[0] | (w[1 % KPT] << 16);
-        }
+        if (KPT == 4) *reinterpret_cast<uint2 *>(vt + off) = make_uint2(w[0], w[1 % (KPT / 2)]);
+        else *reinterpret_cast<uint32_t *>(vt + off) = w[0];
     }
 }
 
@@ -232,19 +233,26 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     for (int i = 0; i < 16; ++i) O[mt][i] *= corr;
             }
             const float mref = (m == -INFINITY) ? 0.f : m;
+            // P in bf16 (the MFMA operand); the row sum adds those same rounded
+            // values (v_dot2 against ones, two chains), so the normalised weights
+            // sum to one exactly as used
             bf16x8_t P[4];
+            const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+            float ls1 = 0.f;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_fast(fmaf(S[s >> 1][8 * (s & 1) + e], scale_log2e, -mref));
-                    lsum += p[e];
-                }
+                for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(S[s >> 1][8 * (s & 1) + e], scale_log2e, -mref));
                 uint4 u = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]),
                                      pack2(p[6], p[7]));
                 P[s] = __builtin_bit_cast(bf16x8_t, u);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.x), one2, lsum, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one2, ls1, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one2, lsum, false);
+                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one2, ls1, false);
             }
+            lsum += ls1;
             // O^T += V^T P^T: k = key in the permuted order of the S^T accumulators
             const char *vt = cur + TL::KBYTES;
 #pragma unroll
