@@ -122,7 +122,7 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
         return RODIMUS_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !(scale < 3.0e38f)) return RODIMUS_ERR_INVALID_ARG;
     if ((long long)B * H * T * (dk > dv ? dk : dv) > (1LL << 46)) return RODIMUS_ERR_INVALID_ARG;
-    if (!swska_supported(dk, dv, dtype)) return RODIMUS_ERR_UNSUPPORTED;
+    if (!swska_supported(T, dk, dv, dtype)) return RODIMUS_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || T == 0) return RODIMUS_OK;
     if (!ok_ptr(q) || !ok_ptr(k_shared) || !ok_ptr(v) || !ok_ptr(o)) return RODIMUS_ERR_INVALID_ARG;
     SkaArgs a{q, k_shared, v, o, B, H, T, dk, dv, window, scale, dtype};

@@ -43,7 +43,7 @@ void launch_decode_step(const DecodeArgs &a, hipStream_t st);
 void launch_scan_generic(const ScanArgs &a, hipStream_t st);
 void launch_scan_mfma(const ScanArgs &a, const ScanPlan &p, hipStream_t st);
 void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st);
-bool swska_supported(int dk, int dv, int dtype);
+bool swska_supported(int T, int dk, int dv, int dtype);
 void launch_swska(const SkaArgs &a, hipStream_t st);
 
 }  // namespace rodimus

@@ -135,7 +135,10 @@ __device__ __forceinline__ const bf16_t *uni_ptr(const bf16_t *p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16_t *base, int T) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)uni_ptr(base), (short)0, uni(T * kD * 2), 0x00020000);
 }
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+// Byte offsets are unsigned 32-bit: rows up to T + 63 (a ragged last chunk)
+// times 256 bytes stay below 2^32 for T < kMaxT, and rows at or past T read
+// zeros (buffer bounds).
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
@@ -159,7 +162,7 @@ __device__ __forceinline__ void load_raw(Raw<C, WITH_Q> &R, const Rsrc &rs, int 
     constexpr int TPR = C / 16;
 #pragma unroll
     for (int tt = 0; tt < TPR; ++tt) {
-        const int off = (t0 + TPR * r + tt) * (kD * 2) + 16 * cg;
+        const uint32_t off = (uint32_t)(t0 + TPR * r + tt) * (kD * 2u) + 16u * cg;
         if (WITH_Q) R.q[tt] = bload(rs.q, off);
         R.k[tt] = bload(rs.k, off);
         R.g[tt] = bload(rs.g, off);
@@ -173,7 +176,7 @@ __device__ __forceinline__ void load_raw(Raw<C, WITH_Q> &R, const Rsrc &rs, int 
 template <int TPR>
 __device__ __forceinline__ void load_one(uint4 (&x)[TPR], __amdgpu_buffer_rsrc_t rs, int t0, int r, int cg) {
 #pragma unroll
-    for (int tt = 0; tt < TPR; ++tt) x[tt] = bload(rs, (t0 + TPR * r + tt) * (kD * 2) + 16 * cg);
+    for (int tt = 0; tt < TPR; ++tt) x[tt] = bload(rs, (uint32_t)(t0 + TPR * r + tt) * (kD * 2u) + 16u * cg);
 }
 
 // Gates and in-chunk inclusive scan: on return l2a holds Lam (inclusive

@@ -67,7 +67,9 @@ template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const bf16_t *base, int T) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)uni_ptr(base), (short)0, uni(T * D * 2), 0x00020000);
 }
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int byte_off) {
+// Byte offsets are unsigned 32-bit: key rows up to T + 63 times D * 2 bytes stay
+// below 2^32 whenever T * D * 2 < 2^31 (the supported range).
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
@@ -89,12 +91,12 @@ __device__ __forceinline__ void fetch_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_b
 #pragma unroll
     for (int i = 0; i < Tile<D>::KVEC; ++i) {
         const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
-        rk[i] = bload(kr, (k0 + row) * D * 2 + 16 * col);
+        rk[i] = bload(kr, (uint32_t)(k0 + row) * (D * 2u) + 16u * col);
     }
     constexpr int KPT = Tile<D>::KPT;
     const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) rv[i] = bload(vr, (k0 + KPT * kg + i) * D * 2 + 16 * dg);
+    for (int i = 0; i < KPT; ++i) rv[i] = bload(vr, (uint32_t)(k0 + KPT * kg + i) * (D * 2u) + 16u * dg);
 }
 
 template <int D>
@@ -286,8 +288,10 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 
 }  // namespace
 
-bool swska_supported(int dk, int dv, int dtype) {
-    return dtype == 1 && dk == dv && (dk == 128 || dk == 64);
+// The key and value descriptors address T rows of dk bf16 with 32-bit byte
+// offsets: T * dk * 2 must stay below 2^31.
+bool swska_supported(int T, int dk, int dv, int dtype) {
+    return dtype == 1 && dk == dv && (dk == 128 || dk == 64) && (long long)T * dk * 2 < (1LL << 31);
 }
 
 void launch_swska(const SkaArgs &a, hipStream_t st) {

@@ -129,8 +129,9 @@ int rodimus_decode_step(const void *q, const void *k, const void *v, const void 
  *   window >= 1 (window >= T is causal attention over the whole prefix).
  *
  * No rotary embedding is applied: pass rotated q and k.  Supported:
- * RODIMUS_BF16 with dk = dv = 128 or dk = dv = 64; other combinations return
- * RODIMUS_ERR_UNSUPPORTED.  B, H, T >= 0.
+ * RODIMUS_BF16 with dk = dv = 128 or dk = dv = 64, and T * dk * 2 < 2^31
+ * (T <= 8388607 at dk = 128, T <= 16777215 at dk = 64); other combinations
+ * return RODIMUS_ERR_UNSUPPORTED.  B, H, T >= 0.
  */
 int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
                 int B, int H, int T, int dk, int dv, int window, float scale, int dtype,

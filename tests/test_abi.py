@@ -119,3 +119,7 @@ def test_swska_unsupported_shapes():
     assert ska(dk=128, dv=64) == rd.ERR_UNSUPPORTED
     assert ska(dk=32, dv=32) == rd.ERR_UNSUPPORTED
     assert ska(dtype=rd.F32) == rd.ERR_UNSUPPORTED
+    # 32-bit byte offsets into k_shared and v: T * dk * 2 < 2^31
+    assert ska(T=1 << 23) == rd.ERR_UNSUPPORTED
+    assert ska(T=1 << 24, dk=64, dv=64) == rd.ERR_UNSUPPORTED
+    assert ska(T=(1 << 30), B=0) == rd.ERR_UNSUPPORTED

@@ -1,0 +1,79 @@
+"""GPU parity at the largest sequence length each bf16 kernel accepts, where
+the 32-bit buffer offsets (T * 256 bytes per tensor) are closest to their
+limit.  Inputs are drawn on the device (workloads.device_normal); the oracle
+reads back the exact bf16 values of the slices it checks.
+
+* Prefill, T = 2^23 - 1 (131072 chunks of 64, a ragged last chunk, 256
+  segments): a reset token 100 positions before the end (g = -40, tau = +40,
+  so a ~ 4e-18 and beta ~ 1) makes the last 100 outputs and S_T depend only on
+  those 100 tokens, so the oracle checks them exactly from S0 = 0.  The first
+  100 outputs are checked from the start of the sequence.
+* SW-SKA, T = 2^23 - 1 at d = 128 (the largest T the entry point supports):
+  rows sampled across the whole sequence, each computed by the oracle from its
+  own window.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_attention_ddts_amd as rd
+import oracle
+import workloads
+from tests.gpu_helpers import TOL, err, host, log
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "g", "theta")
+T_MAX = (1 << 23) - 1
+
+
+def _scan_inputs_on_device(T, seed):
+    s = 1.0 / np.sqrt(128)
+    shp = (1, 1, T, 128)
+    return dict(q=workloads.device_normal(shp, seed, 0.0, s), k=workloads.device_normal(shp, seed + 1, 0.0, s),
+                v=workloads.device_normal(shp, seed + 2), g=workloads.device_normal(shp, seed + 3),
+                theta=workloads.device_normal(shp, seed + 4))
+
+
+def test_prefill_max_T_reset_tail():
+    T, tail = T_MAX, 100
+    log(f"prefill max T={T}: inputs on the device")
+    d = _scan_inputs_on_device(T, 71)
+    tr = T - tail
+    d["g"][0, 0, tr].fill_(-40.0)
+    d["theta"][0, 0, tr].fill_(40.0)
+    log("prefill max T: GPU")
+    o, ST = rd.rodimus_scan_prefill(*(d[n] for n in NAMES), None, 64)
+    torch.cuda.synchronize()
+    log("prefill max T: oracle on the head and the tail")
+    head = [host(d[n][:, :, :tail]) for n in NAMES]
+    ro, _ = oracle.scan(*head, nthreads=1)
+    assert err(host(o[:, :, :tail]), ro) <= TOL["bf16"]
+    tl = [host(d[n][:, :, tr:]) for n in NAMES]
+    ro, rST = oracle.scan(*tl, nthreads=1)
+    eo, es = err(host(o[:, :, tr:]), ro), err(host(ST), rST)
+    log(f"  tail err o {eo:.3e}  S_T {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    # every output finite, checked on the device in slices
+    for c0 in range(0, T, 1 << 21):
+        assert torch.isfinite(o[:, :, c0:c0 + (1 << 21)].float()).all()
+
+
+def test_swska_max_T_sampled_rows():
+    T, w, H = T_MAX, 4096, 1
+    log(f"swska max T={T}: inputs on the device")
+    q = workloads.device_normal((1, H, T, 128), 81, 0.0, 1.0 / np.sqrt(128))
+    k = workloads.device_normal((1, T, 128), 82)
+    v = workloads.device_normal((1, H, T, 128), 83)
+    log("swska max T: GPU")
+    o = rd.sw_ska_attn(q, k, v, w)
+    torch.cuda.synchronize()
+    rows = [0, 1, 4095, 4096, 1 << 22, (1 << 23) - 4097, T - 2, T - 1]
+    log(f"swska max T: oracle on rows {rows}")
+    for t in rows:
+        lo = max(0, t - w + 1)
+        sl = slice(lo, t + 1)
+        ro = oracle.swska(host(q[:, :, sl]), host(k[:, sl]), host(v[:, :, sl]), w, 1.0 / np.sqrt(128),
+                          rows=[t - lo])
+        e = err(host(o[:, :, t]), ro[:, :, t - lo])
+        assert e <= TOL["bf16"], (t, e)

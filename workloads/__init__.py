@@ -115,6 +115,22 @@ def swska_inputs(seed, B, H, T, dk, dv, dtype="bf16", q_sigma=None, k_sigma=1.0,
     return dict(q=q, k=k, v=v)
 
 
+def device_normal(shape, seed, mu=0.0, sigma=1.0, dtype="bf16", device="cuda"):
+    """N(mu, sigma^2) samples drawn on the device, for inputs too large to draw
+    on the host (the maximum-length checks): torch's seeded Philox generator
+    in fp32, then rounded to the storage dtype (nearest even).  Whoever needs
+    exact values (the oracle) reads back the rounded tensor."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    if mu != 0.0:
+        x.add_(mu)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
 # The five workloads, named by what they are.
 CONFIGS = {
     "tiny_fp32_scan": dict(kind="scan", B=1, H=2, T=256, dk=16, dv=32, dtype="fp32", chunk=32,
