@@ -59,11 +59,37 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace (string literals kept), so
+    that editing a comment does not count as changing a kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_hash(kind: str) -> str:
+    """Hash of the code (comments and whitespace removed) of a kernel's sources."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,11 +34,12 @@
 // Kb^T, V^T) while waves 4-7 (consumers) contract chunk k-1 on the matrix cores
 // from the other LDS buffer; one barrier per chunk.  Each consumer wave owns 32
 // of the 128 state columns: its fp32 128x32 state slice lives in MFMA
-// accumulator registers for the whole segment.  The masked score tiles stay in
-// The masked score tiles A^T = Kh Qt^T are built once per chunk (one tile per
-// consumer wave) and exchanged through LDS behind a barrier of the four
-// consumer waves only.  o is produced transposed (o^T = S^T Qt^T + V^T A^T) so
-// that each lane stores 8-byte runs.
+// accumulator registers for the whole segment, and the consumer waves issue at
+// a higher priority than the producers.  The masked score tiles A^T = Kh Qt^T
+// are built once per chunk (the three 32x32 tiles on or below the diagonal for
+// C = 64, one for C = 32, each by one consumer wave) and exchanged through LDS
+// behind a barrier of the four consumer waves only.  o is produced transposed
+// (o^T = S^T Qt^T + V^T A^T) so that each lane stores 8-byte runs.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operand A[m][k] sits in lane m + 32*(k/8),
 // element k%8; B[k][n] in lane n + 32*(k/8), element k%8; the accumulator
