@@ -226,13 +226,26 @@ def bench_copy(nbytes=1 << 30, steps=5):
                 gbs=2 * a.numel() / (ms * 1e-3) / 1e9)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, min_cpu_s=12.0, max_reps=40):
     """The fp64 oracle on the host cores over the whole prefill workload, repeated
     until the process has spent at least min_cpu_s seconds of CPU time (all
-    threads together); the rate is the mean over the repetitions."""
+    threads together); the rate is the mean over the repetitions.  Also timed
+    single-threaded (the plain sequential definition) on one (b,h) pair."""
     import oracle
     import workloads
-    cores = min(os.cpu_count() or 1, 16)
+    nproc = os.cpu_count() or 1
+    cores = min(nproc, 16)
     x = workloads.scan_inputs(cfg["seed"], cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"],
                               cfg["dtype"], gate_mu=cfg["gate_mu"])
     arrs = [x[n].f64() for n in NAMES]
@@ -246,11 +259,19 @@ def cpu_baseline(cfg, min_cpu_s=12.0, max_reps=40):
             break
     dt = time.perf_counter() - t0
     cpu = time.process_time() - c0
+    one = [np.ascontiguousarray(a[:1, :1]) for a in arrs]
+    t1 = time.perf_counter()
+    oracle.scan(*one, nthreads=1)
+    dt1 = time.perf_counter() - t1
     BT = cfg["B"] * cfg["T"]
     return dict(value=round(reps * BT / dt, 1), unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"the whole workload (B={cfg['B']} x T={cfg['T']} tokens x H={cfg['H']} heads, "
                        f"fp64 sequential scan per (b,h) on {cores} threads) run {reps} times: "
-                       f"{dt:.2f} s wall, {cpu:.1f} s CPU")
+                       f"{dt:.2f} s wall, {cpu:.1f} s CPU",
+                single_thread=dict(value=round(cfg["T"] / dt1 / cfg["H"], 1), unit="tokens/s",
+                                   sample=f"one (b,h) pair of T={cfg['T']} tokens on 1 thread, "
+                                          f"{dt1:.3f} s; tokens/s counts a token as all {cfg['H']} heads"),
+                nproc=nproc, cpu_model=_cpu_model())
 
 
 def main():
