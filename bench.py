@@ -56,6 +56,7 @@ KERNEL_SOURCES = {
     "prefill": ("scan_mfma.hip", "device_common.h"),
     "decode": ("decode.hip", "device_common.h"),
     "swska": ("swska.hip", "device_common.h"),
+    "swska_decode": ("swska_decode.hip", "device_common.h"),
 }
 
 
@@ -215,6 +216,43 @@ def bench_swska(cfg, steps, warmup):
                 tflops=flops / (ms * 1e-3) / 1e12, bytes=nbytes)
 
 
+def swska_decode_bytes(N, H, dk, dv, window):
+    # per sequence-step: the shared key window and every head's value window read;
+    # q, k_new, v_new read; the new key/values written to the caches; o written (bf16)
+    return N * (window * dk * 2 + H * window * dv * 2 + H * dk * 2 + 2 * (dk * 2 + H * dv * 2)
+                + H * dv * 2)
+
+
+def bench_swska_decode(cfg, steps, warmup):
+    """Decode steps over full window caches; each step appends one token per
+    sequence (the library advances the positions)."""
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    N, H, dk, dv, W = cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], cfg["window"]
+    kc = workloads.device_normal((N, W, dk), cfg["seed"] * 100 + 1)
+    vc = workloads.device_normal((N, H, W, dv), cfg["seed"] * 100 + 2)
+    pool = workloads.swska_inputs(cfg["seed"], N, H, cfg["pool"], dk, dv)
+    qs, ks, vs = (_dev(pool[n]) for n in ("q", "k", "v"))
+    toks = [(qs[:, :, i].contiguous(), ks[:, i].contiguous(), vs[:, :, i].contiguous())
+            for i in range(cfg["pool"])]
+    pos = torch.full((N,), cfg["pos0"], dtype=torch.int32, device="cuda")
+    o = torch.empty(N, H, dv, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(rd.sw_ska_decode_workspace_bytes(N, H, dk, dv, W), dtype=torch.uint8,
+                     device="cuda")
+    state = {"s": 0}
+
+    def step():
+        qn, kn, vn = toks[state["s"] % len(toks)]
+        state["s"] += 1
+        rd.sw_ska_decode_step(qn, kn, vn, kc, vc, pos, o=o, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    nbytes = swska_decode_bytes(N, H, dk, dv, W)
+    return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+
+
 def bench_copy(nbytes=1 << 30, steps=5):
     """A plain device-to-device copy of known size (counter calibration)."""
     import torch
@@ -281,7 +319,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -303,6 +341,8 @@ def main():
             r = bench_decode(workloads.CONFIGS["decode_N256"], args.steps, args.warmup)
         elif args.only == "swska":
             r = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], args.steps, args.warmup)
+        elif args.only == "swska_decode":
+            r = bench_swska_decode(workloads.CONFIGS["swska_decode_N64_w4096"], args.steps, args.warmup)
         else:
             r = bench_copy()
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
@@ -319,6 +359,9 @@ def main():
     lr = bench_prefill(lc, max(3, args.steps // 4), 1)
     print("bench: swska_T32768_w4096", file=sys.stderr, flush=True)
     sr = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], max(3, args.steps // 4), 1)
+    print("bench: swska_decode_N64_w4096", file=sys.stderr, flush=True)
+    sdc = workloads.CONFIGS["swska_decode_N64_w4096"]
+    sd = bench_swska_decode(sdc, sdc["steps"], 10)
 
     cpu = None
     if not args.no_cpu:
@@ -366,6 +409,12 @@ def main():
                 "roofline": {"bound": "mfma", "achieved": round(sr["tflops"], 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}},
+            "swska_decode_N64_w4096": {
+                "us_per_step": round(sd["us_per_step"], 2), "tokens_per_s": round(sd["tokens_per_s"]),
+                "steps": sd["steps"],
+                "roofline": {"bound": "hbm", "achieved": round(sd["gbs"], 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(sd["gbs"] / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": sd["bytes"]}},
         },
     }
     print(json.dumps(line), flush=True)

@@ -11,6 +11,11 @@ Entry points (same names as the C ABI):
 * :func:`rodimus_decode_step`  -- one recurrent step on a resident state
   (in place by default); returns ``o``.
 * :func:`sw_ska_attn`          -- sliding-window shared-key attention; returns ``o``.
+* :func:`sw_ska_decode_step`   -- one SW-SKA token per sequence over ring-buffer
+  window caches (appends the token, advances ``pos``); returns ``o``.
+
+Every tensor's shape is checked against the others before the call, since the
+C ABI receives bare pointers.
 
 If the shared library has not been built, importing works but every call
 raises ``RuntimeError``; there is no fallback implementation.
@@ -30,7 +35,8 @@ LIB_PATH = os.path.join(_HERE, "librodimus.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 F32, BF16 = 0, 1
 EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill", "rodimus_decode_step",
-            "sw_ska_attn", "rodimus_status_string")
+            "sw_ska_attn", "sw_ska_decode_workspace_bytes", "sw_ska_decode_step",
+            "rodimus_status_string")
 
 _lib = None
 
@@ -58,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.rodimus_decode_step.restype = i
         L.sw_ska_attn.argtypes = [vp] * 4 + [i] * 6 + [ctypes.c_float, i, vp]
         L.sw_ska_attn.restype = i
+        L.sw_ska_decode_workspace_bytes.argtypes = [i] * 6
+        L.sw_ska_decode_workspace_bytes.restype = sz
+        L.sw_ska_decode_step.argtypes = [vp] * 7 + [i] * 5 + [ctypes.c_float, i, vp, sz, vp]
+        L.sw_ska_decode_step.restype = i
         L.rodimus_status_string.argtypes = [i]
         L.rodimus_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -86,6 +96,11 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _shape(t: Optional[torch.Tensor], shape, name: str):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -112,6 +127,15 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
     for x in (k, g, tau, v):
         if x.dtype != q.dtype:
             raise TypeError("q, k, v, g, tau must share one dtype")
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (B, H, T, dk), nm)
+    _shape(v, (B, H, T, dv), "v")
+    _shape(S0, (B, H, dk, dv), "S0")
+    _shape(o, (B, H, T, dv), "o")
+    _shape(S_T, (B, H, dk, dv), "S_T")
+    for x, nm in ((S0, "S0"), (S_T, "S_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if S_T is None and want_state:
@@ -135,6 +159,16 @@ def rodimus_decode_step(q, k, v, g, tau, S_in, S_out=None, *, o=None, stream=Non
     dt = _dtype_code(q)
     if S_out is None:
         S_out = S_in
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (N, H, dk), nm)
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau must share one dtype")
+    _shape(v, (N, H, dv), "v")
+    _shape(S_in, (N, H, dk, dv), "S_in")
+    _shape(S_out, (N, H, dk, dv), "S_out")
+    _shape(o, (N, H, dv), "o")
+    if S_in.dtype != torch.float32 or S_out.dtype != torch.float32:
+        raise TypeError("the state must be float32")
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     st = lib().rodimus_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S_in),
@@ -151,9 +185,53 @@ def sw_ska_attn(q, k_shared, v, window: int, scale: Optional[float] = None, *, o
     dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(dk)
+    _shape(k_shared, (B, T, dk), "k_shared")
+    _shape(v, (B, H, T, dv), "v")
+    _shape(o, (B, H, T, dv), "o")
+    if k_shared.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k_shared, v must share one dtype")
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     st = lib().sw_ska_attn(_ptr(q), _ptr(k_shared), _ptr(v), _ptr(o), B, H, T, dk, dv, int(window),
                            float(scale), dt, _stream(stream))
     _check(st, "sw_ska_attn")
+    return o
+
+
+def sw_ska_decode_workspace_bytes(N, H, dk, dv, window, dtype=BF16) -> int:
+    return int(lib().sw_ska_decode_workspace_bytes(N, H, dk, dv, window, dtype))
+
+
+def sw_ska_decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale: Optional[float] = None, *,
+                       o=None, workspace=None, stream=None) -> torch.Tensor:
+    """q: [N,H,dk]; k_new: [N,dk]; v_new: [N,H,dv]; k_cache: [N,W,dk];
+    v_cache: [N,H,W,dv]; pos: [N] int32 (tokens seen; advanced by one).
+    Writes the token into slot pos mod W of the caches.  Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v_new.shape[-1]
+    W = k_cache.shape[1]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    _shape(k_new, (N, dk), "k_new")
+    _shape(v_new, (N, H, dv), "v_new")
+    _shape(k_cache, (N, W, dk), "k_cache")
+    _shape(v_cache, (N, H, W, dv), "v_cache")
+    _shape(pos, (N,), "pos")
+    _shape(o, (N, H, dv), "o")
+    for x in (k_new, v_new, k_cache, v_cache):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k_new, v_new and the caches must share one dtype")
+    if pos.dtype != torch.int32:
+        raise TypeError("pos must be int32")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    need = sw_ska_decode_workspace_bytes(N, H, dk, dv, W, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sw_ska_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(pos), _ptr(o), N, H, dk, dv, W, float(scale), dt,
+                                  _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "sw_ska_decode_step")
     return o

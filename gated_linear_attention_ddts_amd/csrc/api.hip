@@ -130,4 +130,36 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
     return hip_status();
 }
 
+static bool ska_decode_sizes_ok(int N, int H, int dk, int dv, int window, int dtype) {
+    if (N < 0 || H < 0 || window < 1 || window > (1 << 19)) return false;
+    if (!ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype)) return false;
+    // grids and element counts must fit the kernels' index arithmetic
+    if ((long long)N * H > (1LL << 30) || (long long)N * ((window + 127) / 128) > (1LL << 30)) return false;
+    if ((long long)N * H * window * (dk > dv ? dk : dv) > (1LL << 46)) return false;
+    return true;
+}
+
+size_t sw_ska_decode_workspace_bytes(int N, int H, int dk, int dv, int window, int dtype) {
+    if (!ska_decode_sizes_ok(N, H, dk, dv, window, dtype) || !swska_decode_supported(dk, dv, dtype))
+        return 0;
+    return swska_decode_workspace(N, H, dv, window);
+}
+
+int sw_ska_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                       void *v_cache, int *pos, void *o, int N, int H, int dk, int dv, int window,
+                       float scale, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!ska_decode_sizes_ok(N, H, dk, dv, window, dtype)) return RODIMUS_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !(scale < 3.0e38f)) return RODIMUS_ERR_INVALID_ARG;
+    if (!swska_decode_supported(dk, dv, dtype)) return RODIMUS_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return RODIMUS_OK;
+    if (!ok_ptr(q) || !ok_ptr(k_new) || !ok_ptr(v_new) || !ok_ptr(k_cache) || !ok_ptr(v_cache) ||
+        !ok_ptr(o) || pos == nullptr || ((uintptr_t)pos & 3) != 0)
+        return RODIMUS_ERR_INVALID_ARG;
+    const size_t need = swska_decode_workspace(N, H, dv, window);
+    if (!ok_ptr(workspace) || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
+    SkaDecArgs a{q, k_new, v_new, k_cache, v_cache, pos, o, N, H, dk, dv, window, scale, dtype, workspace};
+    launch_swska_decode(a, (hipStream_t)stream);
+    return hip_status();
+}
+
 }  // extern "C"

@@ -31,6 +31,17 @@ struct SkaArgs {
     int dtype;
 };
 
+struct SkaDecArgs {
+    const void *q, *k_new, *v_new;
+    void *k_cache, *v_cache;
+    int *pos;
+    void *o;
+    int N, H, dk, dv, window;
+    float scale;
+    int dtype;
+    void *workspace;
+};
+
 // Segment plan of the prefill: number of T-segments per (b,h) and workspace.
 struct ScanPlan {
     bool mfma;     // bf16, dk = dv = 128 MFMA kernel
@@ -45,5 +56,8 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &p, hipStream_t st);
 void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st);
 bool swska_supported(int T, int dk, int dv, int dtype);
 void launch_swska(const SkaArgs &a, hipStream_t st);
+bool swska_decode_supported(int dk, int dv, int dtype);
+size_t swska_decode_workspace(int N, int H, int dv, int window);
+void launch_swska_decode(const SkaDecArgs &a, hipStream_t st);
 
 }  // namespace rodimus

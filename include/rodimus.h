@@ -2,14 +2,16 @@
  * rodimus.h -- C ABI of the MI355X (gfx950) Rodimus* token-mixer library
  *              (librodimus.so).
  *
- * The library computes three operations of the Rodimus* token mixer, each in
+ * The library computes the operations of the Rodimus* token mixer, each in
  * hand-written HIP kernels launched asynchronously on the caller's stream:
  *
  *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
  *                        whole prompt, in chunkwise-parallel form;
  *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
  *  sw_ska_attn           sliding-window attention with one key matrix shared
- *                        by all heads (SW-SKA).
+ *                        by all heads (SW-SKA), over a whole sequence;
+ *  sw_ska_decode_step    one SW-SKA token per sequence over ring-buffer
+ *                        window caches.
  *
  * Sources.  The Rodimus block paragraph of "ICLR 2025 | Rodimus*: ..."
  * (CodeFuse article) describes the recurrent state with a selection gate, a
@@ -136,6 +138,41 @@ int rodimus_decode_step(const void *q, const void *k, const void *v, const void 
 int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
                 int B, int H, int T, int dk, int dv, int window, float scale, int dtype,
                 void *stream);
+
+/*
+ * One decode step of SW-SKA for N independent sequences over ring-buffer
+ * window caches (the KV cache that sharing the key shrinks: CodeFuse article,
+ * SKA / Rodimus+ paragraphs and Fig. 4; window semantics as sw_ska_attn).
+ *
+ *   q     : [N, H, dk]   the new token's per-head queries
+ *   k_new : [N, dk]      its key (shared by the heads)
+ *   v_new : [N, H, dv]   its per-head values
+ *   k_cache : [N, window, dk]      v_cache : [N, H, window, dv]
+ *   pos   : [N] int32, device     tokens each sequence has seen (>= 0)
+ *   o     : [N, H, dv]
+ *
+ * Position p of a sequence lives in slot p mod window of both caches.  With
+ * t = pos[n], the step writes k_new / v_new into slot t mod window, computes
+ *
+ *   o[n,h] = sum_{s=max(0,t-window+1)}^{t} softmax_s(scale * q[n,h].k_s) v[n,h,s]
+ *
+ * (row t of sw_ska_attn over the sequence), and then increments pos[n]; all
+ * in stream order.  Slots that hold no position of the window (t + 1 <
+ * window) are never read.  A negative pos is treated as 0.
+ *
+ * Supported: RODIMUS_BF16 with dk = dv = 128 or 64 (else
+ * RODIMUS_ERR_UNSUPPORTED); scale finite and > 0; 1 <= window <= 524288
+ * (else RODIMUS_ERR_INVALID_ARG).  All buffers
+ * are caller-owned device memory, 16-byte aligned (pos: 4-byte aligned).
+ * `workspace` holds per-split partial results: at least
+ * sw_ska_decode_workspace_bytes(N, H, dk, dv, window, dtype) bytes, else
+ * RODIMUS_ERR_INVALID_ARG.  N = 0 or H = 0 is a no-op (pos unchanged).
+ */
+size_t sw_ska_decode_workspace_bytes(int N, int H, int dk, int dv, int window, int dtype);
+int sw_ska_decode_step(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                       void *v_cache, int *pos, void *o, int N, int H, int dk, int dv, int window,
+                       float scale, int dtype, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *rodimus_status_string(int status);

@@ -22,7 +22,7 @@ def declared_functions():
     return sorted(set(n for n in names if n not in ("if", "sizeof")))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_exported_entry_points():
     assert declared_functions() == sorted(rd.EXPORTED)
 
 
@@ -123,3 +123,39 @@ def test_swska_unsupported_shapes():
     assert ska(T=1 << 23) == rd.ERR_UNSUPPORTED
     assert ska(T=1 << 24, dk=64, dv=64) == rd.ERR_UNSUPPORTED
     assert ska(T=(1 << 30), B=0) == rd.ERR_UNSUPPORTED
+
+
+def skadec(**kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, pos=FAKE, o=FAKE, N=2, H=3, dk=128, dv=128,
+             window=256, scale=0.088, dtype=rd.BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rd.lib().sw_ska_decode_step(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["pos"], a["o"],
+                                       a["N"], a["H"], a["dk"], a["dv"], a["window"], a["scale"],
+                                       a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(kn=None), dict(vn=None), dict(kc=None), dict(vc=None), dict(o=None),
+    dict(pos=None), dict(pos=FAKE + 2), dict(q=MISALIGNED), dict(kc=MISALIGNED), dict(ws=None),
+    dict(ws_bytes=16), dict(N=-1), dict(H=-1), dict(window=0), dict(window=-5), dict(dk=7),
+    dict(scale=0.0), dict(scale=float("nan")), dict(scale=float("inf")), dict(dtype=5),
+])
+def test_swska_decode_rejects(kw):
+    assert skadec(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_swska_decode_unsupported_and_empty():
+    assert skadec(dk=128, dv=64) == rd.ERR_UNSUPPORTED
+    assert skadec(dk=32, dv=32) == rd.ERR_UNSUPPORTED
+    assert skadec(dtype=rd.F32) == rd.ERR_UNSUPPORTED
+    assert skadec(N=0, q=None, ws=None) == rd.OK
+    assert skadec(H=0, q=None, ws=None) == rd.OK
+
+
+def test_swska_decode_workspace_query():
+    # per (sequence, head): the window's scores (rounded up to 256 slots), then per
+    # 256-slot split dv outputs + max + sum (+ 2 pad), all fp32
+    assert rd.sw_ska_decode_workspace_bytes(64, 16, 128, 128, 4096) == 64 * 16 * (4096 + 16 * 132) * 4
+    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 100) == 3 * 5 * (256 + 68) * 4
+    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 32, 100) == 0      # unsupported
+    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 0) == 0        # invalid window

@@ -40,3 +40,9 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_swska_decode_bytes_per_sequence_step():
+    # key window + one head's value window, q, k_new, v_new in; k_new, v_new to the caches; o out
+    w, d = 4096, 128
+    assert bench.swska_decode_bytes(1, 1, d, d, w) == 2 * w * d * 2 + d * 2 + 2 * (2 * d * 2) + d * 2

@@ -143,4 +143,8 @@ CONFIGS = {
                         pool=8, seed=4),
     "swska_T32768_w4096": dict(kind="swska", B=1, H=16, T=32768, dk=128, dv=128, window=4096,
                                dtype="bf16", seed=5),
+    # SW-SKA decode: 64 sequences whose 4096-slot window caches are full
+    # (shared K [64, 4096, 128], per-head V [64, 16, 4096, 128]), one token per step
+    "swska_decode_N64_w4096": dict(kind="swska_decode", N=64, H=16, dk=128, dv=128, window=4096,
+                                   pos0=8192, steps=200, pool=8, dtype="bf16", seed=6),
 }
