@@ -414,6 +414,7 @@ def main():
                 "steps": sd["steps"],
                 "roofline": {"bound": "hbm", "achieved": round(sd["gbs"], 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(sd["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("swska_decode_N64_w4096", "swska_decode"),
                              "algorithmic_bytes": sd["bytes"]}},
         },
     }
