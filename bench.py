@@ -186,9 +186,35 @@ def bench_decode(cfg, steps, warmup):
         rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], S, o=o)
 
     ms = _time(step, steps, warmup)
+    ms_graph = _graph_time(step, len(dsets), 8)
     nbytes = decode_bytes(N, H, dk, dv)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3)
+
+
+def _graph_time(step, n_capture, replays):
+    """Per-step GPU time (ms) of `step` captured n_capture times into one HIP
+    graph and replayed: what a serving loop without per-step launches sees."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(n_capture):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_capture):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * n_capture)
 
 
 def swska_pairs(T, w):
@@ -248,9 +274,10 @@ def bench_swska_decode(cfg, steps, warmup):
         rd.sw_ska_decode_step(qn, kn, vn, kc, vc, pos, o=o, workspace=ws)
 
     ms = _time(step, steps, warmup)
+    ms_graph = _graph_time(step, len(toks), 4)
     nbytes = swska_decode_bytes(N, H, dk, dv, W)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps)
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3)
 
 
 def bench_copy(nbytes=1 << 30, steps=5):
@@ -393,6 +420,7 @@ def main():
                      "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "decode": {"workload": "decode_N256", "us_per_step": round(dec["us_per_step"], 2),
+                   "us_per_step_graph": round(dec["us_per_step_graph"], 2),
                    "tokens_per_s": round(dec["tokens_per_s"]), "steps": dec["steps"],
                    "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -411,6 +439,7 @@ def main():
                              "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}},
             "swska_decode_N64_w4096": {
                 "us_per_step": round(sd["us_per_step"], 2), "tokens_per_s": round(sd["tokens_per_s"]),
+                "us_per_step_graph": round(sd["us_per_step_graph"], 2),
                 "steps": sd["steps"],
                 "roofline": {"bound": "hbm", "achieved": round(sd["gbs"], 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(sd["gbs"] / HBM_PEAK_GBS, 4),
