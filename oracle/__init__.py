@@ -51,6 +51,8 @@ def _load():
         lib.oracle_scan.argtypes = [ctypes.c_int] * 5 + [dp] * 6 + [dp, dp, ctypes.c_int]
         lib.oracle_scan.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_int] * 4 + [dp] * 6 + [dp, dp]
+        lib.oracle_scan_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14 + [ctypes.c_int]
+        lib.oracle_scan_backward.restype = ctypes.c_int
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_swska.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double] + [dp] * 4 +
                                      [ctypes.POINTER(ctypes.c_longlong), ctypes.c_longlong,
@@ -99,6 +101,32 @@ def scan(q, k, v, g, theta, S0=None, nthreads: int = 1):
                              _ptr(S0), _ptr(o), _ptr(ST), int(nthreads))
     assert rc == 0
     return o, ST
+
+
+def scan_backward(q, k, v, g, theta, dO, S0=None, dST=None, nthreads: int = 1):
+    """Gradients of sum(dO * o) + sum(dST * S_T) of the sequential recurrence
+    with respect to q, k, v, g, theta and S0.  Returns a dict of fp64 arrays
+    dq, dk, dv, dg, dtheta (shaped like the inputs) and dS0 [B,H,dk,dv]."""
+    q, k, v, g, theta, dO = (_f64(x) for x in (q, k, v, g, theta, dO))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for x in (k, g, theta):
+        assert x.shape == q.shape
+    assert v.shape == (B, H, T, dv) and dO.shape == (B, H, T, dv)
+    if S0 is not None:
+        S0 = _f64(S0)
+        assert S0.shape == (B, H, dk, dv)
+    if dST is not None:
+        dST = _f64(dST)
+        assert dST.shape == (B, H, dk, dv)
+    out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v), dg=np.empty_like(g),
+               dtheta=np.empty_like(theta), dS0=np.empty((B, H, dk, dv)))
+    rc = _load().oracle_scan_backward(B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                      _ptr(theta), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(out["dq"]),
+                                      _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                      _ptr(out["dtheta"]), _ptr(out["dS0"]), int(nthreads))
+    assert rc == 0
+    return out
 
 
 def decode(q, k, v, g, theta, S):

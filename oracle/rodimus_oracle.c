@@ -143,6 +143,142 @@ int oracle_scan(int B, int H, int T, int dk, int dv,
     return 0;
 }
 
+/* --------------------------------------------------- the scan, backward */
+
+/* Gradients of L = sum(dO * o) + sum(dST * S_T) with respect to every input
+ * of the scan, by reverse-mode differentiation of the definition above:
+ *   S_t = diag(a_t) S_{t-1} + (beta_t * k_t)^T v_t,   o_t = q_t S_t.
+ * With G_t the gradient of L with respect to S_t (G_T = dST, or 0):
+ *   G_t    += q_t^T dO_t                       (o_t reads S_t)
+ *   dq_t    = dO_t S_t^T
+ *   da_t    = rowsum(G_t * S_{t-1}),   d(beta*k)_t = G_t v_t^T,   dv_t = (beta_t*k_t) G_t
+ *   G_{t-1} = diag(a_t) G_t,           dS0 = G_0.
+ * Gate chain rule (a = exp(-sigmoid(theta) softplus(-g)),
+ * beta = exp(-sigmoid(theta) softplus(g)); sigmoid' = sigmoid(x) sigmoid(-x),
+ * softplus' = sigmoid):
+ *   da/dg     =  a    * sigmoid(theta) sigmoid(-g)
+ *   dbeta/dg  = -beta * sigmoid(theta) sigmoid(g)
+ *   da/dth    = -a    * sigmoid(theta) sigmoid(-theta) softplus(-g)
+ *   dbeta/dth = -beta * sigmoid(theta) sigmoid(-theta) softplus(g)
+ * All states S_0 .. S_T of a pair are kept (fp64), so memory is
+ * (T + 1) * dk * dv doubles per thread. */
+typedef struct {
+    int B, H, T, dk, dv;
+    const double *q, *k, *v, *g, *theta, *S0, *dO, *dST;
+    double *dq, *dk_, *dv_, *dg, *dtheta, *dS0;
+    int next;
+    pthread_mutex_t lock;
+} bwd_job;
+
+static void bwd_one(const bwd_job *J, int bh, double *Sall, double *a, double *beta, double *G,
+                    double *dbk) {
+    const int T = J->T, dk = J->dk, dv = J->dv;
+    const size_t xoff = (size_t)bh * T * dk, voff = (size_t)bh * T * dv;
+    const size_t soff = (size_t)bh * dk * dv, ss = (size_t)dk * dv;
+    /* forward, keeping every state: Sall[t] = S_t, S_0 = S0 */
+    if (J->S0) memcpy(Sall, J->S0 + soff, sizeof(double) * ss);
+    else memset(Sall, 0, sizeof(double) * ss);
+    for (int t = 0; t < T; ++t) {
+        const double *kt = J->k + xoff + (size_t)t * dk;
+        const double *gt = J->g + xoff + (size_t)t * dk, *ht = J->theta + xoff + (size_t)t * dk;
+        const double *vt = J->v + voff + (size_t)t * dv;
+        double *at = a + (size_t)t * dk, *bt = beta + (size_t)t * dk;
+        for (int i = 0; i < dk; ++i) {
+            double la, lb;
+            oracle_gates(gt + i, ht + i, 1, &la, &lb);
+            at[i] = exp(la);
+            bt[i] = exp(lb);
+        }
+        const double *Sp = Sall + (size_t)t * ss;
+        double *Sn = Sall + (size_t)(t + 1) * ss;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                Sn[i * dv + j] = at[i] * Sp[i * dv + j] + bt[i] * kt[i] * vt[j];
+    }
+    /* reverse */
+    if (J->dST) memcpy(G, J->dST + soff, sizeof(double) * ss);
+    else memset(G, 0, sizeof(double) * ss);
+    for (int t = T - 1; t >= 0; --t) {
+        const double *qt = J->q + xoff + (size_t)t * dk, *kt = J->k + xoff + (size_t)t * dk;
+        const double *gt = J->g + xoff + (size_t)t * dk, *ht = J->theta + xoff + (size_t)t * dk;
+        const double *vt = J->v + voff + (size_t)t * dv, *dOt = J->dO + voff + (size_t)t * dv;
+        const double *St = Sall + (size_t)(t + 1) * ss, *Sp = Sall + (size_t)t * ss;
+        const double *at = a + (size_t)t * dk, *bt = beta + (size_t)t * dk;
+        double *dqt = J->dq + xoff + (size_t)t * dk, *dkt = J->dk_ + xoff + (size_t)t * dk;
+        double *dgt = J->dg + xoff + (size_t)t * dk, *dht = J->dtheta + xoff + (size_t)t * dk;
+        double *dvt = J->dv_ + voff + (size_t)t * dv;
+        /* o_t = q_t S_t */
+        for (int i = 0; i < dk; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < dv; ++j) acc += dOt[j] * St[i * dv + j];
+            dqt[i] = acc;
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) G[i * dv + j] += qt[i] * dOt[j];
+        /* S_t = diag(a_t) S_{t-1} + (beta_t k_t)^T v_t */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += bt[i] * kt[i] * G[i * dv + j];
+            dvt[j] = acc;
+        }
+        for (int i = 0; i < dk; ++i) {
+            double da = 0.0, d_bk = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                da += G[i * dv + j] * Sp[i * dv + j];
+                d_bk += G[i * dv + j] * vt[j];
+            }
+            dbk[i] = d_bk;
+            dkt[i] = bt[i] * d_bk;
+            const double dbeta = kt[i] * d_bk;
+            const double st = sigmoid(ht[i]), sg = sigmoid(gt[i]), sgm = sigmoid(-gt[i]);
+            const double stm = sigmoid(-ht[i]);
+            dgt[i] = da * at[i] * st * sgm - dbeta * bt[i] * st * sg;
+            dht[i] = -st * stm * (da * at[i] * softplus(-gt[i]) + dbeta * bt[i] * softplus(gt[i]));
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) G[i * dv + j] *= at[i];
+    }
+    if (J->dS0) memcpy(J->dS0 + soff, G, sizeof(double) * ss);
+}
+
+static void *bwd_worker(void *arg) {
+    bwd_job *J = (bwd_job *)arg;
+    const size_t ss = (size_t)J->dk * J->dv;
+    double *Sall = (double *)malloc(sizeof(double) * ss * (J->T + 1));
+    double *a = (double *)malloc(sizeof(double) * ((size_t)J->T * J->dk + 1));
+    double *beta = (double *)malloc(sizeof(double) * ((size_t)J->T * J->dk + 1));
+    double *G = (double *)malloc(sizeof(double) * ss);
+    double *dbk = (double *)malloc(sizeof(double) * J->dk);
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int bh = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (bh >= J->B * J->H) break;
+        bwd_one(J, bh, Sall, a, beta, G, dbk);
+    }
+    free(Sall); free(a); free(beta); free(G); free(dbk);
+    return NULL;
+}
+
+int oracle_scan_backward(int B, int H, int T, int dk, int dv,
+                         const double *q, const double *k, const double *v,
+                         const double *g, const double *theta, const double *S0,
+                         const double *dO, const double *dST,
+                         double *dq, double *dk_, double *dv_, double *dg, double *dtheta,
+                         double *dS0, int nthreads) {
+    if (B <= 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
+    bwd_job J = {B, H, T, dk, dv, q, k, v, g, theta, S0, dO, dST,
+                 dq, dk_, dv_, dg, dtheta, dS0, 0, PTHREAD_MUTEX_INITIALIZER};
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > B * H) nthreads = B * H;
+    if (nthreads == 1) { bwd_worker(&J); return 0; }
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, bwd_worker, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    return 0;
+}
+
 /* ------------------------------------------------------------- the decode */
 
 /* One recurrent step for N independent sequences: the same update as one

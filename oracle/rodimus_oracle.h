@@ -26,6 +26,17 @@ int oracle_scan(int B, int H, int T, int dk, int dv,
                 const double *g, const double *theta, const double *S0,
                 double *o, double *ST, int nthreads);
 
+/* Gradients of sum(dO * o) + sum(dST * S_T) with respect to q, k, v, g, theta
+ * and S0 (reverse-mode through the definition).  S0, dST may be NULL (zeros);
+ * dS0 may be NULL (not returned).  dO: [B,H,T,dv]; outputs shaped like the
+ * inputs. */
+int oracle_scan_backward(int B, int H, int T, int dk, int dv,
+                         const double *q, const double *k, const double *v,
+                         const double *g, const double *theta, const double *S0,
+                         const double *dO, const double *dST,
+                         double *dq, double *dk_, double *dv_, double *dg, double *dtheta,
+                         double *dS0, int nthreads);
+
 /* One recurrent step on N x H states; S_out may alias S_in. */
 int oracle_decode(int N, int H, int dk, int dv,
                   const double *q, const double *k, const double *v,

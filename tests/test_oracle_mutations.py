@@ -14,6 +14,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_backward_pins as bpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "rodimus_oracle.c")
@@ -35,6 +36,8 @@ PIN_TESTS = [
     lambda: pins.test_swska_full_window_is_causal_sdpa(),
     lambda: pins.test_swska_window_one_is_identity(),
     lambda: pins.test_swska_constant_key_is_window_mean(),
+    lambda: bpins.test_backward_matches_central_differences(True),
+    lambda: bpins.test_backward_reduces_to_linear_attention_gradients(),
 ]
 
 MUTATIONS = {
@@ -60,6 +63,14 @@ MUTATIONS = {
     "attention_scale_dropped": ("p[s - s0] = J->scale * acc;", "p[s - s0] = acc;"),
     "attention_shared_key_per_head": ("const double *kb = J->k + (size_t)b * T * dk;",
                                       "const double *kb = J->k + (size_t)(bh % J->B) * T * dk;"),
+    "bwd_decay_grad_uses_new_state": ("da += G[i * dv + j] * Sp[i * dv + j];",
+                                      "da += G[i * dv + j] * St[i * dv + j];"),
+    "bwd_state_grad_not_decayed": ("G[i * dv + j] *= at[i];", "G[i * dv + j] *= 1.0;"),
+    "bwd_dg_sign": ("dgt[i] = da * at[i] * st * sgm - dbeta * bt[i] * st * sg;",
+                    "dgt[i] = da * at[i] * st * sgm + dbeta * bt[i] * st * sg;"),
+    "bwd_dq_previous_state": ("for (int j = 0; j < dv; ++j) acc += dOt[j] * St[i * dv + j];",
+                              "for (int j = 0; j < dv; ++j) acc += dOt[j] * Sp[i * dv + j];"),
+    "bwd_dk_missing_beta": ("dkt[i] = bt[i] * d_bk;", "dkt[i] = d_bk;"),
 }
 
 
@@ -81,7 +92,7 @@ def _build_variant(tmp_path, old=None, new=None):
 def _use(path):
     real = oracle._load()
     lib = ctypes.CDLL(path)
-    for name in ("oracle_gates", "oracle_scan", "oracle_decode", "oracle_swska"):
+    for name in ("oracle_gates", "oracle_scan", "oracle_decode", "oracle_swska", "oracle_scan_backward"):
         getattr(lib, name).argtypes = getattr(real, name).argtypes
         getattr(lib, name).restype = getattr(real, name).restype
     oracle._lib = lib
