@@ -8,6 +8,8 @@ Entry points (same names as the C ABI):
 
 * :func:`rodimus_scan_prefill` -- chunkwise-parallel prefill of the DDTS-gated
   recurrence; returns ``(o, S_T)``.
+* :func:`rodimus_scan_backward` -- gradients of the prefill with respect to q, k,
+  v, g, tau and S0 (fp32); returns a dict.
 * :func:`rodimus_decode_step`  -- one recurrent step on a resident state
   (in place by default); returns ``o``.
 * :func:`sw_ska_attn`          -- sliding-window shared-key attention; returns ``o``.
@@ -34,7 +36,8 @@ LIB_PATH = os.path.join(_HERE, "librodimus.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 F32, BF16 = 0, 1
-EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill", "rodimus_decode_step",
+EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill",
+            "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward", "rodimus_decode_step",
             "sw_ska_attn", "sw_ska_decode_workspace_bytes", "sw_ska_decode_step",
             "rodimus_status_string")
 
@@ -60,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.rodimus_scan_prefill_workspace_bytes.restype = sz
         L.rodimus_scan_prefill.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
         L.rodimus_scan_prefill.restype = i
+        L.rodimus_scan_backward_workspace_bytes.argtypes = [i] * 6
+        L.rodimus_scan_backward_workspace_bytes.restype = sz
+        L.rodimus_scan_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
+        L.rodimus_scan_backward.restype = i
         L.rodimus_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
         L.rodimus_decode_step.restype = i
         L.sw_ska_attn.argtypes = [vp] * 4 + [i] * 6 + [ctypes.c_float, i, vp]
@@ -149,6 +156,47 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
                                     _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "rodimus_scan_prefill")
     return o, S_T
+
+
+def rodimus_scan_backward_workspace_bytes(B, H, T, dk, dv, dtype=BF16) -> int:
+    return int(lib().rodimus_scan_backward_workspace_bytes(B, H, T, dk, dv, dtype))
+
+
+def rodimus_scan_backward(q, k, v, g, tau, dO, S0=None, dS_T=None, *, want_dS0: bool = True,
+                          workspace=None, stream=None) -> dict:
+    """Gradients of sum(dO * o) + sum(dS_T * S_T) of rodimus_scan_prefill with
+    respect to q, k, v, g, tau (shaped like them) and S0 ([B,H,dk,dv]), all
+    float32.  Returns dict(dq, dk, dv, dg, dtau, dS0)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (B, H, T, dk), nm)
+    _shape(v, (B, H, T, dv), "v")
+    _shape(dO, (B, H, T, dv), "dO")
+    _shape(S0, (B, H, dk, dv), "S0")
+    _shape(dS_T, (B, H, dk, dv), "dS_T")
+    for x in (k, g, tau, v, dO):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau, dO must share one dtype")
+    for x, nm in ((S0, "S0"), (dS_T, "dS_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = dict(dq=torch.empty((B, H, T, dk), **f32), dk=torch.empty((B, H, T, dk), **f32),
+               dv=torch.empty((B, H, T, dv), **f32), dg=torch.empty((B, H, T, dk), **f32),
+               dtau=torch.empty((B, H, T, dk), **f32),
+               dS0=torch.empty((B, H, dk, dv), **f32) if want_dS0 else None)
+    need = rodimus_scan_backward_workspace_bytes(B, H, T, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rodimus_scan_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S0), _ptr(dO),
+                                     _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                     _ptr(out["dg"]), _ptr(out["dtau"]), _ptr(out["dS0"]), B, H, T, dk,
+                                     dv, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "rodimus_scan_backward")
+    return out
 
 
 def rodimus_decode_step(q, k, v, g, tau, S_in, S_out=None, *, o=None, stream=None) -> torch.Tensor:

@@ -95,6 +95,40 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
     return hip_status();
 }
 
+size_t rodimus_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+    if (!scan_sizes_ok(B, H, T, dk, dv, 0, dtype)) return 0;
+    return scan_bwd_workspace(B, H, T, dk, dv);
+}
+
+int rodimus_scan_backward(const void *q, const void *k, const void *v, const void *g,
+                          const void *tau, const float *S0, const void *dO, const float *dS_T,
+                          float *dq, float *dk_, float *dv_, float *dg, float *dtau, float *dS0,
+                          int B, int H, int T, int dk, int dv, int dtype,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (!scan_sizes_ok(B, H, T, dk, dv, 0, dtype)) return RODIMUS_ERR_INVALID_ARG;
+    if (!ok_opt_ptr(S0) || !ok_opt_ptr(dS_T) || !ok_opt_ptr(dS0) || !ok_opt_ptr(workspace))
+        return RODIMUS_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (B == 0 || H == 0) return RODIMUS_OK;
+    const size_t nstate = (size_t)B * H * dk * dv;
+    if (T == 0) {  // nothing but the final-state gradient flows back to S0
+        if (dS0) {
+            launch_state_copy(dS_T, dS0, nstate, st);
+            return hip_status();
+        }
+        return RODIMUS_OK;
+    }
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(dO) ||
+        !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
+        return RODIMUS_ERR_INVALID_ARG;
+    const size_t need = scan_bwd_workspace(B, H, T, dk, dv);
+    if (workspace == nullptr || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
+    ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, B, H, T, dk, dv, dtype,
+                  workspace};
+    launch_scan_bwd(a, st);
+    return hip_status();
+}
+
 int rodimus_decode_step(const void *q, const void *k, const void *v, const void *g,
                         const void *tau, const float *S_in, float *S_out, void *o,
                         int N, int H, int dk, int dv, int dtype, void *stream) {

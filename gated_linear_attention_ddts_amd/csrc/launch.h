@@ -15,6 +15,17 @@ struct ScanArgs {
     size_t workspace_bytes;
 };
 
+struct ScanBwdArgs {
+    const void *q, *k, *v, *g, *tau;
+    const float *S0;   // nullable
+    const void *dO;
+    const float *dS_T; // nullable
+    float *dq, *dk_, *dv_, *dg, *dtau;
+    float *dS0;        // nullable
+    int B, H, T, dk, dv, dtype;
+    void *workspace;
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *g, *tau;
     const float *S_in;
@@ -54,6 +65,8 @@ void launch_decode_step(const DecodeArgs &a, hipStream_t st);
 void launch_scan_generic(const ScanArgs &a, hipStream_t st);
 void launch_scan_mfma(const ScanArgs &a, const ScanPlan &p, hipStream_t st);
 void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st);
+size_t scan_bwd_workspace(int B, int H, int T, int dk, int dv);
+void launch_scan_bwd(const ScanBwdArgs &a, hipStream_t st);
 bool swska_supported(int T, int dk, int dv, int dtype);
 void launch_swska(const SkaArgs &a, hipStream_t st);
 bool swska_decode_supported(int dk, int dv, int dtype);

@@ -7,6 +7,7 @@
  *
  *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
  *                        whole prompt, in chunkwise-parallel form;
+ *  rodimus_scan_backward its gradients with respect to every input;
  *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
  *  sw_ska_attn           sliding-window attention with one key matrix shared
  *                        by all heads (SW-SKA), over a whole sequence;
@@ -101,6 +102,31 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
                          const void *tau, const float *S0, void *o, float *S_T,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward of rodimus_scan_prefill: the gradients of
+ *     L = sum(dO * o) + sum(dS_T * S_T)
+ * with respect to q, k, v, g, tau and S0, for the same recurrence and gate map
+ * (reverse-mode through the chunkwise form, chunks of 32 tokens; fp32
+ * arithmetic).  Inputs as for rodimus_scan_prefill, plus
+ *   dO   : [B, H, T, dv] in the input dtype
+ *   dS_T : [B, H, dk, dv] fp32, or NULL (no gradient of the final state)
+ * Outputs, all fp32 and caller-allocated:
+ *   grad_q, grad_k, grad_g, grad_tau : [B, H, T, dk]    grad_v : [B, H, T, dv]
+ *   grad_S0 : [B, H, dk, dv], or NULL (not returned)
+ * S0 NULL means zeros, as in the forward.  Supported: fp32 or bf16 inputs,
+ * dk and dv multiples of 16 up to 128 (else RODIMUS_ERR_INVALID_ARG).
+ * `workspace` (state checkpoints and state gradients, 2*B*H*ceil(T/32)*dk*dv
+ * fp32) must hold rodimus_scan_backward_workspace_bytes(...) bytes, else
+ * RODIMUS_ERR_INVALID_ARG.  T = 0 copies dS_T (or zeros) into grad_S0.
+ */
+size_t rodimus_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
+int rodimus_scan_backward(const void *q, const void *k, const void *v, const void *g,
+                          const void *tau, const float *S0, const void *dO, const float *dS_T,
+                          float *grad_q, float *grad_k, float *grad_v, float *grad_g,
+                          float *grad_tau, float *grad_S0,
+                          int B, int H, int T, int dk, int dv, int dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent (decode) step for N independent sequences (CodeFuse article,

@@ -159,3 +159,37 @@ def test_swska_decode_workspace_query():
     assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 100) == 3 * 5 * (256 + 68) * 4
     assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 32, 100) == 0      # unsupported
     assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 0) == 0        # invalid window
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE, dk_=FAKE,
+             dv_=FAKE, dg=FAKE, dtau=FAKE, dS0=FAKE, B=1, H=2, T=40, dk=16, dv=32, dtype=rd.BF16,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_backward(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S0"], a["dO"],
+                                          a["dST"], a["dq"], a["dk_"], a["dv_"], a["dg"], a["dtau"],
+                                          a["dS0"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                          a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(g=None), dict(tau=None), dict(dO=None),
+    dict(dq=None), dict(dk_=None), dict(dv_=None), dict(dg=None), dict(dtau=None),
+    dict(q=MISALIGNED), dict(S0=MISALIGNED), dict(dST=MISALIGNED), dict(dS0=MISALIGNED),
+    dict(ws=MISALIGNED), dict(ws=None), dict(ws_bytes=2 * 2 * 16 * 32 * 4 * 2 - 4),
+    dict(B=-1), dict(H=-1), dict(T=-1), dict(dk=8), dict(dk=144), dict(dv=0), dict(dtype=2),
+])
+def test_scan_backward_rejects(kw):
+    assert bwd(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_scan_backward_empty_and_workspace():
+    assert bwd(B=0, q=None, ws=None) == rd.OK
+    assert bwd(H=0, dq=None, ws=None) == rd.OK
+    assert bwd(T=0, dS0=None, q=None, ws=None) == rd.OK     # nothing requested
+    # two fp32 [dk,dv] states per (batch, head, 32-token chunk): forward checkpoints
+    # and reverse-carried state gradients
+    assert rd.rodimus_scan_backward_workspace_bytes(1, 2, 40, 16, 32) == 2 * 2 * 2 * 16 * 32 * 4
+    assert rd.rodimus_scan_backward_workspace_bytes(4, 16, 4096, 128, 128) == 2 * 64 * 128 * 128 * 128 * 4
+    assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 0, 128, 128) == 0
+    assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 64, 8, 128) == 0   # invalid dk
