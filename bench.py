@@ -1,7 +1,7 @@
 """Benchmark of the Rodimus* token-mixer hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--only all|prefill|decode|long|swska|copy]
+                    [--only all|prefill|decode|long|swska|swska_decode|backward|copy]
 
 A step is one rodimus_scan_prefill call over the 1.6B-shaped prefill batch
 (B=4, T=4096, H=16, dk=dv=128, bf16 inputs, fp32 state, C=64) with every input
@@ -9,7 +9,8 @@ already resident in HBM; value = B*T / step time (prefill tokens/s).  The
 decode state update (256 sequences x 16 heads, fp32 128x128 states, in-place
 steps cycling over 8 resident input sets) is timed in the same run and
 reported as HBM GB/s and fraction of peak, as the metric asks.  The
-long-context prefill (T=131072) and SW-SKA (T=32768, w=4096) are timed as
+long-context prefill (T=131072), SW-SKA (T=32768, w=4096), the SW-SKA decode
+step and the backward of the prefill scan (same 1.6B batch) are timed as
 extras.
 
 Timing: W untimed warm-up steps, then K steps between two HIP events on the
@@ -20,7 +21,9 @@ combination, the output pass); the roofline entry is for that whole call.
 Algorithmic bytes: prefill, per token-head, q, k, g, tau (4 x 256 B) + v (256 B)
 in and o (256 B) out = 1536 B, plus the fp32 final state; decode, per head, the
 fp32 state read and written (2 x 64 KiB) plus 5 x 256 B of inputs and 256 B of
-output; SW-SKA, q, v, o per token-head and the shared k per token.  Peaks: HBM
+output; SW-SKA, q, v, o per token-head and the shared k per token; backward,
+per token-head, q, k, g, tau, v, dO in (bf16, 6 x 256 B) and dq, dk, dg, dtau,
+dv out (fp32, 5 x 512 B) = 4096 B, plus the fp32 dS0.  Peaks: HBM
 8 TB/s; dense bf16 MFMA 2.5 PFLOP/s.
 
 "traffic" is the HBM byte count per call measured with rocprofv3 counters
@@ -53,10 +56,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 NAMES = ("q", "k", "v", "g", "theta")
 CSRC = os.path.join(ROOT, "gated_linear_attention_ddts_amd", "csrc")
 KERNEL_SOURCES = {
-    "prefill": ("scan_mfma.hip", "device_common.h"),
+    "prefill": ("scan_mfma.hip", "mfma_common.h", "device_common.h"),
     "decode": ("decode.hip", "device_common.h"),
     "swska": ("swska.hip", "device_common.h"),
     "swska_decode": ("swska_decode.hip", "device_common.h"),
+    "backward": ("scan_bwd_mfma.hip", "scan_bwd_body.h", "mfma_common.h", "device_common.h"),
 }
 
 
@@ -163,6 +167,43 @@ def bench_prefill(cfg, steps, warmup):
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
                 gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
                 workspace_bytes=nws)
+
+
+def backward_bytes(B, H, T, dk, dv):
+    # in: q, k, g, tau, v, dO (bf16); out: dq, dk, dg, dtau, dv (fp32); plus dS0 (fp32)
+    return B * H * T * ((4 * dk + 2 * dv) * 2 + (4 * dk + dv) * 4) + B * H * dk * dv * 4
+
+
+def backward_flops(B, H, T, dk, dv, C=32):
+    # per token-head: five dk x dv products (state checkpoint, state gradient,
+    # S dO^T, G v^T, Kb G) and the causal-triangle intra-chunk terms (dP, A,
+    # dq, dk over dk or dv channels, dv over dv)
+    return B * H * T * (10 * dk * dv + (C + 1) * (3 * dk + 2 * dv))
+
+
+def bench_backward(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    B, H, T, dk, dv = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"]
+    x = workloads.scan_inputs(cfg["seed"], B, H, T, dk, dv, cfg["dtype"], gate_mu=cfg["gate_mu"])
+    d = {n: _dev(x[n]) for n in NAMES}
+    del x
+    dO = workloads.device_normal((B, H, T, dv), cfg["seed"] + 1000)
+    ws = torch.empty(rd.rodimus_scan_backward_workspace_bytes(B, H, T, dk, dv, rd.BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        # the binding allocates the five gradient tensors per call from torch's
+        # caching allocator (no device synchronisation)
+        rd.rodimus_scan_backward(d["q"], d["k"], d["v"], d["g"], d["theta"], dO, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    nbytes = backward_bytes(B, H, T, dk, dv)
+    flops = backward_flops(B, H, T, dk, dv)
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
+                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+                workspace_bytes=ws.numel())
 
 
 def decode_bytes(N, H, dk, dv):
@@ -346,7 +387,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "backward", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -370,6 +411,8 @@ def main():
             r = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], args.steps, args.warmup)
         elif args.only == "swska_decode":
             r = bench_swska_decode(workloads.CONFIGS["swska_decode_N64_w4096"], args.steps, args.warmup)
+        elif args.only == "backward":
+            r = bench_backward(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup)
         else:
             r = bench_copy()
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
@@ -389,6 +432,8 @@ def main():
     print("bench: swska_decode_N64_w4096", file=sys.stderr, flush=True)
     sdc = workloads.CONFIGS["swska_decode_N64_w4096"]
     sd = bench_swska_decode(sdc, sdc["steps"], 10)
+    print("bench: backward_1p6b_T4096", file=sys.stderr, flush=True)
+    bw = bench_backward(cfg, max(5, args.steps // 2), 2)
 
     cpu = None
     if not args.no_cpu:
@@ -445,6 +490,14 @@ def main():
                              "unit": "GB/s", "frac": round(sd["gbs"] / HBM_PEAK_GBS, 4),
                              "traffic": measured_traffic("swska_decode_N64_w4096", "swska_decode"),
                              "algorithmic_bytes": sd["bytes"]}},
+            "backward_1p6b_T4096": {
+                "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"]),
+                "roofline": {"bound": "hbm", "achieved": round(bw["gbs"], 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(bw["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("backward_1p6b_T4096", "backward"),
+                             "kernel": "rodimus_scan_backward call (state passes + combine + "
+                             "gradients + fallback)", "algorithmic_bytes": bw["bytes"],
+                             "workspace_bytes": bw["workspace_bytes"]}},
         },
     }
     print(json.dumps(line), flush=True)

@@ -97,6 +97,7 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
 
 size_t rodimus_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
     if (!scan_sizes_ok(B, H, T, dk, dv, 0, dtype)) return 0;
+    if (scan_bwd_mfma_supported(T, dk, dv, dtype)) return scan_bwd_mfma_workspace(B, H, T);
     return scan_bwd_workspace(B, H, T, dk, dv);
 }
 
@@ -121,11 +122,13 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(dO) ||
         !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
         return RODIMUS_ERR_INVALID_ARG;
-    const size_t need = scan_bwd_workspace(B, H, T, dk, dv);
+    const bool mfma = scan_bwd_mfma_supported(T, dk, dv, dtype);
+    const size_t need = mfma ? scan_bwd_mfma_workspace(B, H, T) : scan_bwd_workspace(B, H, T, dk, dv);
     if (workspace == nullptr || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
     ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, B, H, T, dk, dv, dtype,
                   workspace};
-    launch_scan_bwd(a, st);
+    if (mfma) launch_scan_bwd_mfma(a, st);
+    else launch_scan_bwd(a, st);
     return hip_status();
 }
 

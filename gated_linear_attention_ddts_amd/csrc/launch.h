@@ -67,6 +67,9 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &p, hipStream_t st);
 void launch_state_copy(const float *S0, float *S_T, size_t n, hipStream_t st);
 size_t scan_bwd_workspace(int B, int H, int T, int dk, int dv);
 void launch_scan_bwd(const ScanBwdArgs &a, hipStream_t st);
+bool scan_bwd_mfma_supported(int T, int dk, int dv, int dtype);
+size_t scan_bwd_mfma_workspace(int B, int H, int T);
+void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st);
 bool swska_supported(int T, int dk, int dv, int dtype);
 void launch_swska(const SkaArgs &a, hipStream_t st);
 bool swska_decode_supported(int dk, int dv, int dtype);

@@ -1,0 +1,808 @@
+// scan_bwd_mfma.hip -- backward of the chunked DDTS-gated scan on gfx950
+// matrix cores (bf16 inputs, dk = dv = 128; fp32 gradients, fp32 state
+// arithmetic, bf16 matrix-core operands).
+//
+// The per-chunk gradient formulas are those of scan_bwd_body.h (CodeFuse
+// article, Rodimus block paragraph: S_t = diag(a_t) S_{t-1} + (beta_t k_t)^T v_t,
+// o_t = q_t S_t).  Here the intra-chunk pairwise weights are factored as
+// 2^{Lam_i} * 2^{mu_j - Lam_j} (base-2 units, Lam = in-chunk inclusive
+// cumulative log2 a, mu = log2 beta), so that every product is a matrix-core
+// contraction.  With Qt = q 2^{Lam}, Kh = k 2^{mu - Lam}, Kb = Kh 2^{Gam}, S
+// the state entering a 32-token chunk and G the gradient of the state leaving
+// it:
+//     dP  = tril(dO V^T)          A  = tril(Qt Kh^T)
+//     dq  = 2^{Lam} (dP Kh + dO S^T)
+//     dk  = 2^{mu-Lam} (dP^T Qt) + 2^{mu+Gam-Lam} (V G^T)
+//     dv  = A^T dO + Kb G
+//     dLam = q dq - k dk,  dmu = k dk,
+//     dGam = sum_j Kb_j (V G^T)_j + 2^{Gam} rowsum(G * S),
+//     dlam_t = sum_{t' >= t} dLam_t' + dGam,
+// then the gate chain rule (natural-log gradients; 2^{x/ln 2} = e^x).  A chunk
+// whose decay span exceeds kSpan2 would overflow Kh; such chunks are listed and
+// handed to the exact pairwise routine of scan_bwd_body.h.
+//
+// Kernels:
+//   bwd_state_kernel    the state (forward order) and its gradient (reverse
+//                       order) per segment of 64-token chunks, on matrix cores;
+//                       writes a bf16 checkpoint of each at every 64 tokens:
+//                       S entering the chunk, and G leaving it in both
+//                       orientations, all in fragment order (frag_index), so
+//                       that the gradient kernel loads them as ready operands.
+//                       Segments start from zero (the first from S0, the last
+//                       from dS_T); each writes its fp32 edge state and total
+//                       decay.
+//   bwd_combine_kernel  (several segments only) runs the segment edges across
+//                       the sequence: the true state entering and gradient
+//                       leaving each segment (fragment order, bf16), and dS0.
+//                       A checkpoint c of segment s is completed on load as
+//                       S_c = S_loc_c + diag(2^{D_c}) S_in(s).
+//   bwd_grad_kernel     one workgroup per 32-token half of a checkpoint
+//                       interval; the half that does not start at a checkpoint
+//                       bridges to it through the other half (S through the
+//                       first half, G back through the second), then runs all
+//                       products above on the matrix cores and the element-wise
+//                       epilogue in the producer-lane layout.  Two workgroups
+//                       per CU; the two halves of an interval run on one XCD.
+//   bwd_fallback_kernel the listed wide-span halves, with the exact routine.
+#include "launch.h"
+#include "mfma_common.h"
+#include "scan_bwd_body.h"
+
+namespace rodimus {
+
+namespace {
+
+constexpr int kCk = 64;              // tokens per checkpoint interval
+constexpr int kSub = 32;             // tokens per gradient workgroup
+constexpr int kFrag = 32 * 64 * 8;   // bf16 per 128x128 matrix in fragment order (32 KiB)
+constexpr int kT32 = 32 + 8;         // bf16 per transposed LDS row of 32 tokens (+16 B)
+constexpr int kQR = kD + 8;          // bf16 per token row [t][128] (+16 B)
+constexpr int kSR = kD + 4;          // fp32 per staging row (+16 B)
+constexpr int kSlowWG = 256;         // fallback workgroups (one fp32 S/G scratch pair each)
+constexpr int kMaxT = 1 << 23;       // 32-bit buffer offsets (T * 256 bytes)
+constexpr int kCUs = 256;
+
+struct P {
+    const bf16_t *q, *k, *v, *g, *th, *dO;
+    const float *S0, *dST;
+    float *dq, *dk, *dv, *dg, *dth, *dS0;
+    bf16_t *ckS, *ckG, *ckGT;     // [BH][nck] checkpoints, fragment order
+    float *sigS, *sigG;           // [BH][nck][128] 2^{log2 decay to / from the segment edge}
+    float *segS, *segG;           // [BH][nseg][128][128] fp32 segment edge states (row-major)
+    float *segDS, *segDG;         // [BH][nseg][128] total log2 decay of each segment
+    bf16_t *fixS, *fixG, *fixGT;  // [BH][nseg] incoming state / outgoing gradient, fragment order
+    int *bad;                     // [0] = count, then entries bh * (2 nck) + half index
+    float *slot;                  // [kSlowWG][2][128][128] fallback scratch
+    int BH, T, nck, nseg, seg_ck;
+};
+
+// ------------------------------------------------------------ state passes
+// Role 0: S (forward over the segment); role 1: G (reverse), in 32-token steps
+// with a checkpoint at every 64-token boundary.  Wave w keeps the transposed
+// 128 x 32 slice X^T[n][32w..32w+31] (rows n = value channel) in
+// accumulators; role 1 also keeps G[r][32w..32w+31] (rows r = key channel) for
+// the second orientation of the checkpoint.
+constexpr int kStS = 32;   // tokens per state step
+__global__ __launch_bounds__(256, 2)
+void bwd_state_kernel(P p) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * kD * kT32 * 2 + kD * 4];
+    char *sX = smem, *sY = smem + kD * kT32 * 2;
+    float *sGam = reinterpret_cast<float *>(smem + 2 * kD * kT32 * 2);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+    const int nwg = p.BH * p.nseg;
+    const bool rev = (int)blockIdx.x >= nwg;
+    const int id = rev ? (int)blockIdx.x - nwg : (int)blockIdx.x;
+    const int bh = uni(id % p.BH), seg = uni(id / p.BH);
+    if (blockIdx.x == 0 && tid == 0) p.bad[0] = 0;
+    const int c_lo = seg * p.seg_ck, c_hi = min(p.nck, c_lo + p.seg_ck);
+    const size_t rowbase = (size_t)bh * p.T;
+    const int r = l & 15, cg = (w << 2) | (l >> 4);
+    const int rr = 32 * w + l32;  // key channel of this lane's transposed columns (role 1: also n of G)
+
+    Rsrc rs;  // X operand tensor (k or q) in .k, Y operand tensor (v or dO) in .v
+    rs.k = rsrc((rev ? p.q : p.k) + rowbase * kD, p.T);
+    rs.v = rsrc((rev ? p.dO : p.v) + rowbase * kD, p.T);
+    rs.g = rsrc(p.g + rowbase * kD, p.T);
+    rs.th = rsrc(p.th + rowbase * kD, p.T);
+    rs.q = rs.k;
+
+    f32x16_t A[4], B[4];
+    const float *init = rev ? (seg == p.nseg - 1 && p.dST ? p.dST + (size_t)bh * kD * kD : nullptr)
+                            : (seg == 0 && p.S0 ? p.S0 + (size_t)bh * kD * kD : nullptr);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (init) x = *reinterpret_cast<const float4 *>(init + rr * kD + 32 * q + 8 * a4 + 4 * h);
+            A[q][4 * a4 + 0] = x.x; A[q][4 * a4 + 1] = x.y; A[q][4 * a4 + 2] = x.z; A[q][4 * a4 + 3] = x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            B[q][i] = (rev && init) ? init[(32 * q + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + rr] : 0.f;
+    }
+    float dacc = 0.f;  // log2 decay between the segment edge and the current step, channel rr
+
+    Raw<kStS, false> R;
+    const int nst = 2 * (c_hi - c_lo);
+    const int st_first = rev ? 2 * c_hi - 1 : 2 * c_lo;
+    load_raw<kStS, false>(R, rs, st_first * kStS, r, cg);
+    for (int it = 0; it < nst; ++it) {
+        const int stp = rev ? st_first - it : st_first + it;
+        const int t0 = stp * kStS;
+        if ((stp & 1) == (rev ? 1 : 0)) {
+            // checkpoint: S entering chunk c (role 0) / G leaving it (role 1)
+            const size_t ck = (size_t)bh * p.nck + (stp >> 1);
+            bf16_t *dA = (rev ? p.ckG : p.ckS) + ck * kFrag;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                *reinterpret_cast<bf16x8_t *>(dA + ((8 * w + s) * 64 + l) * 8) = cvt8(A[s >> 1], 8 * (s & 1));
+            if (rev) {
+                bf16_t *dB = p.ckGT + ck * kFrag;
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    *reinterpret_cast<bf16x8_t *>(dB + ((8 * w + s) * 64 + l) * 8) = cvt8(B[s >> 1], 8 * (s & 1));
+            }
+            if (h == 0) (rev ? p.sigG : p.sigS)[ck * kD + rr] = exp2_fast(dacc);
+        }
+
+        // operands: X^T (Kb or Qt) and Y^T (V or dO), tokens in permuted order
+        float l2a[2][8], l2b[2][8], lend[8];
+        gates_scan<kStS, false>(R, t0, p.T, r, l, l2a, l2b, lend);
+        float xT[8][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float xf[8];
+            unpack8(R.k[tt], xf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                xT[e][tt] = xf[e] * exp2_fast(rev ? l2a[tt][e] : l2b[tt][e] + lend[e] - l2a[tt][e]);
+        }
+        store_vt<2, kT32>(sY, cg, r, R.v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_t_rows<2, kT32>(sX, 8 * cg + e, r, xT[e]);
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sGam[8 * cg + e] = lend[e];
+        }
+        if (it + 1 < nst) load_raw<kStS, false>(R, rs, (rev ? stp - 1 : stp + 1) * kStS, r, cg);
+        __syncthreads();
+
+        // A (X^T layout): columns rr decay by 2^{Gam[rr]}; A += Y^T X
+        const float gr = sGam[rr];
+        dacc += gr;
+        const float er = exp2_fast(gr);
+        const bf16x8_t xB0 = lds16(sX, (rr * kT32 + 8 * h) * 2), xB1 = lds16(sX, (rr * kT32 + 16 + 8 * h) * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            A[q] *= er;
+            A[q] = mfma(lds16(sY, ((32 * q + l32) * kT32 + 8 * h) * 2), xB0, A[q]);
+            A[q] = mfma(lds16(sY, ((32 * q + l32) * kT32 + 16 + 8 * h) * 2), xB1, A[q]);
+        }
+        if (rev) {
+            // B (rows = key channel): rows decay; B += X^T Y
+            const bf16x8_t yB0 = lds16(sY, (rr * kT32 + 8 * h) * 2), yB1 = lds16(sY, (rr * kT32 + 16 + 8 * h) * 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const float4 gm = *reinterpret_cast<const float4 *>(sGam + 32 * q + 8 * a4 + 4 * h);
+                    B[q][4 * a4 + 0] *= exp2_fast(gm.x); B[q][4 * a4 + 1] *= exp2_fast(gm.y);
+                    B[q][4 * a4 + 2] *= exp2_fast(gm.z); B[q][4 * a4 + 3] *= exp2_fast(gm.w);
+                }
+                B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 8 * h) * 2), yB0, B[q]);
+                B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 16 + 8 * h) * 2), yB1, B[q]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // segment edge: local end state (role 0) / local entering gradient (role 1)
+    float *edge;
+    if (p.nseg == 1) {
+        if (!rev || !p.dS0) return;
+        edge = p.dS0 + (size_t)bh * kD * kD;  // one segment: the gradient entering it is dS0
+    } else {
+        const size_t sb = (size_t)bh * p.nseg + seg;
+        edge = (rev ? p.segG : p.segS) + sb * kD * kD;
+        if (h == 0) (rev ? p.segDG : p.segDS)[sb * kD + rr] = dacc;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+            *reinterpret_cast<float4 *>(edge + rr * kD + 32 * q + 8 * a4 + 4 * h) =
+                make_float4(A[q][4 * a4 + 0], A[q][4 * a4 + 1], A[q][4 * a4 + 2], A[q][4 * a4 + 3]);
+}
+
+// ----------------------------------------------------------------- combine
+// One thread per (b,h, r, n): the state entering each segment (left to right)
+// and the gradient leaving each segment (right to left), stored bf16 in
+// fragment order for the gradient kernel; the gradient entering segment 0 is
+// dS0.
+__global__ __launch_bounds__(256)
+void bwd_combine_kernel(P p) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)p.BH * kD * kD) return;
+    const int bh = (int)(idx >> 14), e = (int)(idx & 16383), r = e >> 7, n = e & 127;
+    const int fi = frag_index(r, n), fiT = frag_index(n, r);
+    float S = 0.f;
+    for (int s = 0; s < p.nseg; ++s) {
+        const size_t sb = (size_t)bh * p.nseg + s;
+        if (s > 0) p.fixS[sb * kFrag + fi] = f2bf(S);
+        S = fmaf(exp2_fast(p.segDS[sb * kD + r]), S, p.segS[sb * kD * kD + e]);
+    }
+    float G = 0.f;
+    for (int s = p.nseg - 1; s >= 0; --s) {
+        const size_t sb = (size_t)bh * p.nseg + s;
+        if (s < p.nseg - 1) {
+            p.fixG[sb * kFrag + fi] = f2bf(G);
+            p.fixGT[sb * kFrag + fiT] = f2bf(G);
+        }
+        G = fmaf(exp2_fast(p.segDG[sb * kD + r]), G, p.segG[sb * kD * kD + e]);
+    }
+    if (p.dS0) p.dS0[idx] = G;
+}
+
+// ---------------------------------------------------------- gradient kernel
+// LDS (bytes).  Token rows [32][136] bf16 (channels permuted): Qt, Kh, Kb, dO,
+// V; transposed rows [128][40] bf16 (tokens permuted): Qt^T, Kh^T, dO^T; fp32
+// Gam of this half and of the bridged half, the decay term, the sigma of the
+// G^T fix-up.  The bridge operands alias Qt^T / Kh^T (written after the
+// bridge); the fp32 staging of the epilogue aliases all operand rows.
+constexpr int kRowB = kSub * kQR * 2;           // 8704
+constexpr int kTB = kD * kT32 * 2;              // 10240
+constexpr int kOffQr = 0, kOffKr = kRowB, kOffKbr = 2 * kRowB, kOffDOr = 3 * kRowB, kOffVr = 4 * kRowB;
+constexpr int kOffQT = 5 * kRowB, kOffKT = kOffQT + kTB, kOffDOT = kOffKT + kTB;
+constexpr int kOffGam = kOffDOT + kTB, kOffGamB = kOffGam + kD * 4, kOffDec = kOffGamB + kD * 4;
+constexpr int kOffSig = kOffDec + kD * 4;
+constexpr int kGradLDS = kOffSig + kD * 4;
+constexpr int kOffB1 = kOffQT, kOffB2 = kOffKT;
+static_assert(4 * kSub * kSR * 4 <= kOffGam, "staging fits in the dead operand rows");
+static_assert(kGradLDS <= 80 * 1024, "two workgroups per CU");
+
+__device__ __forceinline__ void ld_frag(const bf16_t *base, int f, int l, float (&x)[8]) {
+    unpack8(*reinterpret_cast<const uint4 *>(base + ((size_t)f * 64 + l) * 8), x);
+}
+__device__ __forceinline__ bf16x8_t pack_frag(const float (&x)[8]) {
+    return __builtin_bit_cast(bf16x8_t, make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]),
+                                                   pack2(x[4], x[5]), pack2(x[6], x[7])));
+}
+__device__ __forceinline__ float bf_round(float x) { return lo_bf(pack2(x, 0.f)); }
+
+// Bridge of the first half to its checkpoint would be the identity; each
+// workgroup's own half is (c, half), the bridged one the other half of c.
+__global__ __launch_bounds__(256, 2)
+void bwd_grad_kernel(P p) {
+    __shared__ __attribute__((aligned(16))) char smem[kGradLDS];
+    float *sGam = reinterpret_cast<float *>(smem + kOffGam);
+    float *sGamB = reinterpret_cast<float *>(smem + kOffGamB);
+    float *sDec = reinterpret_cast<float *>(smem + kOffDec);
+    float *sSig = reinterpret_cast<float *>(smem + kOffSig);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
+    // block -> (interval, half); the two halves of an interval share blockIdx % 8 (one XCD)
+    const int pair = (int)(blockIdx.x >> 4) * 8 + (int)(blockIdx.x & 7);
+    const int half = (blockIdx.x >> 3) & 1;
+    if (pair >= p.BH * p.nck) return;
+    const int bh = uni(pair / p.nck), c = uni(pair % p.nck);
+    const int tc = c * kCk, t0 = tc + kSub * half;
+    if (t0 >= p.T) return;
+    const int seg = c / p.seg_ck;
+    const bool fixS = seg > 0, fixG = seg < p.nseg - 1;
+    const size_t rowbase = (size_t)bh * p.T;
+    const size_t ck = (size_t)bh * p.nck + c, sb = (size_t)bh * p.nseg + seg;
+    const int r = l & 15, cg = (w << 2) | (l >> 4);
+    const int rr = 32 * w + l32;
+
+    const __amdgpu_buffer_rsrc_t rq = rsrc(p.q + rowbase * kD, p.T), rk = rsrc(p.k + rowbase * kD, p.T);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + rowbase * kD, p.T), rg = rsrc(p.g + rowbase * kD, p.T);
+    const __amdgpu_buffer_rsrc_t rth = rsrc(p.th + rowbase * kD, p.T), rdo = rsrc(p.dO + rowbase * kD, p.T);
+
+    // this half's inputs, and the other half's for the bridge (tokens past T read 0)
+    uint4 Rq[2], Rk[2], Rv[2], Rg[2], Rth[2], Rdo[2], Bx[2], By[2], Bg[2], Bth[2];
+    const int ts = half ? tc : tc + kSub;
+    load_one<2>(Rg, rg, t0, r, cg);
+    load_one<2>(Rth, rth, t0, r, cg);
+    load_one<2>(Rq, rq, t0, r, cg);
+    load_one<2>(Rk, rk, t0, r, cg);
+    load_one<2>(Rv, rv, t0, r, cg);
+    load_one<2>(Rdo, rdo, t0, r, cg);
+    load_one<2>(Bg, rg, ts, r, cg);
+    load_one<2>(Bth, rth, ts, r, cg);
+    if (half) {
+        load_one<2>(Bx, rk, ts, r, cg);
+        load_one<2>(By, rv, ts, r, cg);
+    } else {
+        load_one<2>(Bx, rq, ts, r, cg);
+        load_one<2>(By, rdo, ts, r, cg);
+    }
+
+    // this half's gates; span check (Kh = k 2^{mu - Lam} must stay finite)
+    uint32_t qTp[8], kTp[8];  // Qt^T / Kh^T rows of this lane's 8 channels, 2 tokens packed
+    {
+        float l2a[2][8], l2b[2][8], lend[8];
+        gates_scan_gt<kSub>(Rg, Rth, t0, p.T, r, l, l2a, l2b, lend);
+        bool bad = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bad |= lend[e] < -kSpan2;
+        if (__syncthreads_or(bad)) {
+            if (tid == 0) {
+                const int i = atomicAdd(p.bad, 1);
+                p.bad[1 + i] = bh * (2 * p.nck) + 2 * c + half;
+            }
+            return;
+        }
+        // token-row operands and dO^T
+        float qT[8][2], kT[8][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float qf[8], kf[8], qt[8], kh[8], kb[8];
+            unpack8(Rq[tt], qf);
+            unpack8(Rk[tt], kf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qt[e] = qf[e] * exp2_fast(l2a[tt][e]);
+                kh[e] = kf[e] * exp2_fast(l2b[tt][e] - l2a[tt][e]);
+                kb[e] = kf[e] * exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e]);
+                qT[e][tt] = qt[e];
+                kT[e][tt] = kh[e];
+            }
+            const int t = 2 * r + tt;
+            store_q_row<kQR>(smem + kOffQr, t, cg, qt);
+            store_q_row<kQR>(smem + kOffKr, t, cg, kh);
+            store_q_row<kQR>(smem + kOffKbr, t, cg, kb);
+            store_raw_row<kQR>(smem + kOffDOr, t, cg, Rdo[tt]);
+            store_raw_row<kQR>(smem + kOffVr, t, cg, Rv[tt]);
+        }
+        store_vt<2, kT32>(smem + kOffDOT, cg, r, Rdo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qTp[e] = pack2(qT[e][0], qT[e][1]);
+            kTp[e] = pack2(kT[e][0], kT[e][1]);
+        }
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sGam[8 * cg + e] = lend[e];
+        }
+    }
+    // bridge operands: first half -> Kb0^T, V0^T (the state through it);
+    // second half -> Qt1^T, dO1^T (the gradient back through it)
+    {
+        float l2a[2][8], l2b[2][8], lend[8];
+        gates_scan_gt<kSub>(Bg, Bth, ts, p.T, r, l, l2a, l2b, lend);
+        float xT[8][2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            float xf[8];
+            unpack8(Bx[tt], xf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                xT[e][tt] = xf[e] * exp2_fast(half ? l2b[tt][e] + lend[e] - l2a[tt][e] : l2a[tt][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_t_rows<2, kT32>(smem + kOffB1, 8 * cg + e, r, xT[e]);
+        store_vt<2, kT32>(smem + kOffB2, cg, r, By);
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sGamB[8 * cg + e] = lend[e];
+        }
+    }
+    if (fixG && tid < kD) sSig[tid] = p.sigG[ck * kD + tid];
+    __syncthreads();
+
+    auto rowf = [&](int off, int row, int s) { return lds16(smem, off + (row * kQR + 16 * s + 8 * h) * 2); };
+    auto trf = [&](int off, int row, int ks) { return lds16(smem, off + (row * kT32 + 16 * ks + 8 * h) * 2); };
+
+    // S entering and G (both orientations) leaving this half, bf16 operands
+    bf16x8_t Sf[8], Gf[8], GTf[8];
+    const float sigS = fixS ? p.sigS[ck * kD + rr] : 0.f;
+    const float sigG = fixG ? sSig[rr] : 0.f;
+    const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag, *cGT = p.ckGT + ck * kFrag;
+    const bf16_t *xS = p.fixS + sb * kFrag, *xG = p.fixG + sb * kFrag, *xGT = p.fixGT + sb * kFrag;
+    if (half) {
+        // S through the first half: diag(2^{Gam0}) S_c + Kb0^T V0 (transposed accumulators)
+        const float eg = exp2_fast(sGamB[rr]);
+        f32x16_t A[4];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float x[8], y[8];
+            ld_frag(cS, 8 * w + s, l, x);
+            if (fixS) {
+                ld_frag(xS, 8 * w + s, l, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigS, y[e], x[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) A[q] = mfma(trf(kOffB2, 32 * q + l32, ks), trf(kOffB1, rr, ks), A[q]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) Sf[s] = cvt8(A[s >> 1], 8 * (s & 1));
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float x[8], y[8];
+            ld_frag(cG, 8 * w + s, l, x);
+            if (fixG) {
+                ld_frag(xG, 8 * w + s, l, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigG, y[e], x[e]);
+            }
+            Gf[s] = pack_frag(x);
+            ld_frag(cGT, 8 * w + s, l, x);
+            if (fixG) {
+                ld_frag(xGT, 8 * w + s, l, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
+            }
+            GTf[s] = pack_frag(x);
+        }
+    } else {
+        // G back through the second half: diag(2^{Gam1}) G_c + Qt1^T dO1, both
+        // orientations, one after the other
+        {
+            f32x16_t A[4];
+            const float eg = exp2_fast(sGamB[rr]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                float x[8], y[8];
+                ld_frag(cG, 8 * w + s, l, x);
+                if (fixG) {
+                    ld_frag(xG, 8 * w + s, l, y);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = fmaf(sigG, y[e], x[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) A[q] = mfma(trf(kOffB2, 32 * q + l32, ks), trf(kOffB1, rr, ks), A[q]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) Gf[s] = cvt8(A[s >> 1], 8 * (s & 1));
+        }
+        {
+            f32x16_t B[4];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                float x[8], y[8];
+                ld_frag(cGT, 8 * w + s, l, x);
+                if (fixG) {
+                    ld_frag(xGT, 8 * w + s, l, y);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    B[s >> 1][8 * (s & 1) + e] = x[e] * exp2_fast(sGamB[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) B[q] = mfma(trf(kOffB1, 32 * q + l32, ks), trf(kOffB2, rr, ks), B[q]);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) GTf[s] = cvt8(B[s >> 1], 8 * (s & 1));
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            float x[8], y[8];
+            ld_frag(cS, 8 * w + s, l, x);
+            if (fixS) {
+                ld_frag(xS, 8 * w + s, l, y);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigS, y[e], x[e]);
+            }
+            Sf[s] = pack_frag(x);
+        }
+    }
+
+    // ---- matrix-core products (wave w: output columns 32w..32w+31) ----
+    // dv = A^T dO + Kb G (rows j, column rr), straight to memory
+    {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = mfma(rowf(kOffQr, l32, s), rowf(kOffKr, l32, s), acc);   // A[i][j]
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (l32 > 8 * (i >> 2) + 4 * h + (i & 3)) acc[i] = 0.f;
+        const bf16x8_t opA0 = cvt8(acc, 0), opA1 = cvt8(acc, 8);
+        f32x16_t av = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) av = mfma(rowf(kOffKbr, l32, s), GTf[s], av);
+        av = mfma(opA0, trf(kOffDOT, rr, 0), av);
+        av = mfma(opA1, trf(kOffDOT, rr, 1), av);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = 8 * (i >> 2) + 4 * h + (i & 3);
+            if (t0 + j < p.T) p.dv[(rowbase + t0 + j) * kD + rr] = av[i];
+        }
+    }
+    __syncthreads();  // bridge operands are dead: Qt^T, Kh^T take their place
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        *reinterpret_cast<uint32_t *>(smem + kOffQT + ((8 * cg + e) * kT32 + perm16(2 * r)) * 2) = qTp[e];
+        *reinterpret_cast<uint32_t *>(smem + kOffKT + ((8 * cg + e) * kT32 + perm16(2 * r)) * 2) = kTp[e];
+    }
+    // V G^T, and the decay term rowsum(G * S) of key channel rr
+    f32x16_t ax = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) ax = mfma(rowf(kOffVr, l32, s), Gf[s], ax);
+    float dec = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        float a8[8], b8[8];
+        unpack_frag(Sf[s], a8);
+        unpack_frag(Gf[s], b8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dec = fmaf(a8[e], b8[e], dec);
+    }
+    dec += __shfl_xor(dec, 32);
+    // dO S^T
+    f32x16_t a1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a1 = mfma(rowf(kOffDOr, l32, s), Sf[s], a1);
+    // dP (rows i, columns j) and dP^T, masked to j <= i
+    bf16x8_t opP[2], opPT[2];
+    {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = mfma(rowf(kOffDOr, l32, s), rowf(kOffVr, l32, s), acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (l32 > 8 * (i >> 2) + 4 * h + (i & 3)) acc[i] = 0.f;
+        opP[0] = cvt8(acc, 0); opP[1] = cvt8(acc, 8);
+        acc = f32x16_t{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) acc = mfma(rowf(kOffVr, l32, s), rowf(kOffDOr, l32, s), acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + 4 * h + (i & 3) > l32) acc[i] = 0.f;
+        opPT[0] = cvt8(acc, 0); opPT[1] = cvt8(acc, 8);
+    }
+    __syncthreads();  // Qt^T, Kh^T written
+    // in-chunk parts: dP Kh and dP^T Qt
+    f32x16_t aI = {}, kI = {};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        aI = mfma(opPT[ks], trf(kOffKT, rr, ks), aI);
+        kI = mfma(opP[ks], trf(kOffQT, rr, ks), kI);
+    }
+    // the epilogue's inputs again (L2-resident)
+    uint4 Eq[2], Ek[2], Eg[2], Eth[2];
+    load_one<2>(Eq, rq, t0, r, cg);
+    load_one<2>(Ek, rk, t0, r, cg);
+    load_one<2>(Eg, rg, t0, r, cg);
+    load_one<2>(Eth, rth, t0, r, cg);
+    __syncthreads();  // operand rows are dead: stage the accumulators
+    float *sQI = reinterpret_cast<float *>(smem), *sQ1 = sQI + kSub * kSR, *sKI = sQ1 + kSub * kSR,
+          *sX2 = sKI + kSub * kSR;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = 8 * (i >> 2) + 4 * h + (i & 3);
+        sQI[t * kSR + rr] = aI[i];
+        sQ1[t * kSR + rr] = a1[i];
+        sKI[t * kSR + rr] = kI[i];
+        sX2[t * kSR + rr] = ax[i];
+    }
+    if (h == 0) sDec[rr] = dec;
+    __syncthreads();
+
+    // ---- epilogue, producer layout: tokens 2r, 2r+1, channels 8cg..8cg+7 ----
+    // The in-chunk parts of dLam use the same bf16-rounded Qt, Kh as the
+    // products, so that their reverse cumulative sum telescopes exactly.
+    float l2a[2][8], l2b[2][8], lend[8];
+    gates_scan_gt<kSub>(Eg, Eth, t0, p.T, r, l, l2a, l2b, lend);
+    float dlam[2][8], dmu[2][8], ebs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ebs[e] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * r + tt;
+        float qi[8], q1[8], ki[8], xa[8], qf[8], kf[8], dqv[8], dkv[8];
+        const float *rows[4] = {sQI + t * kSR + 8 * cg, sQ1 + t * kSR + 8 * cg, sKI + t * kSR + 8 * cg,
+                                sX2 + t * kSR + 8 * cg};
+        float *dst[4] = {qi, q1, ki, xa};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            *reinterpret_cast<float4 *>(dst[a]) = *reinterpret_cast<const float4 *>(rows[a]);
+            *reinterpret_cast<float4 *>(dst[a] + 4) = *reinterpret_cast<const float4 *>(rows[a] + 4);
+        }
+        unpack8(Eq[tt], qf);
+        unpack8(Ek[tt], kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float eq = exp2_fast(l2a[tt][e]), ekh = exp2_fast(l2b[tt][e] - l2a[tt][e]);
+            const float ekb = exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e]);
+            const float qt = bf_round(qf[e] * eq), kh = bf_round(kf[e] * ekh);
+            const float kbx = kf[e] * ekb * xa[e];
+            dqv[e] = eq * (qi[e] + q1[e]);
+            dkv[e] = fmaf(ekh, ki[e], ekb * xa[e]);
+            dlam[tt][e] = fmaf(qt, qi[e], -kh * ki[e]) + fmaf(qf[e] * eq, q1[e], -kbx);
+            dmu[tt][e] = kf[e] * dkv[e];
+            ebs[e] += kbx;
+        }
+        if (t0 + t < p.T) {
+            float *oq = p.dq + (rowbase + t0 + t) * kD + 8 * cg, *ok = p.dk + (rowbase + t0 + t) * kD + 8 * cg;
+            *reinterpret_cast<float4 *>(oq) = make_float4(dqv[0], dqv[1], dqv[2], dqv[3]);
+            *reinterpret_cast<float4 *>(oq + 4) = make_float4(dqv[4], dqv[5], dqv[6], dqv[7]);
+            *reinterpret_cast<float4 *>(ok) = make_float4(dkv[0], dkv[1], dkv[2], dkv[3]);
+            *reinterpret_cast<float4 *>(ok + 4) = make_float4(dkv[4], dkv[5], dkv[6], dkv[7]);
+        }
+    }
+    float dl[2][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float x = ebs[e];  // sum over the 16 lanes of the row: all 32 tokens
+        x += row_shr<1>(x);
+        x += row_shr<2>(x);
+        x += row_shr<4>(x);
+        x += row_shr<8>(x);
+        const float dG = bcast_lane(x, (l & 48) | 15) + exp2_fast(lend[e]) * sDec[8 * cg + e];
+        // reverse inclusive cumulative sum of dLam over the 32 tokens
+        const float s1 = dlam[1][e], s0 = dlam[0][e] + s1;
+        float y = s0;
+        y += row_shl<1>(y);
+        y += row_shl<2>(y);
+        y += row_shl<4>(y);
+        y += row_shl<8>(y);
+        const float later = row_shl<1>(y);  // tokens of the lanes after this one
+        dl[1][e] = s1 + later + dG;
+        dl[0][e] = s0 + later + dG;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * r + tt;
+        if (t0 + t >= p.T) continue;
+        float gf[8], tf[8], dgv[8], dtv[8];
+        unpack8(Eg[tt], gf);
+        unpack8(Eth[tt], tf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ddts_gate_grads(gf[e], tf[e], dl[tt][e], dmu[tt][e], dgv[e], dtv[e]);
+        float *og = p.dg + (rowbase + t0 + t) * kD + 8 * cg, *ot = p.dth + (rowbase + t0 + t) * kD + 8 * cg;
+        *reinterpret_cast<float4 *>(og) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
+        *reinterpret_cast<float4 *>(og + 4) = make_float4(dgv[4], dgv[5], dgv[6], dgv[7]);
+        *reinterpret_cast<float4 *>(ot) = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
+        *reinterpret_cast<float4 *>(ot + 4) = make_float4(dtv[4], dtv[5], dtv[6], dtv[7]);
+    }
+}
+
+// --------------------------------------------------------------- fallback
+// Listed halves, exactly: rebuild S entering and G leaving the half in fp32
+// (row-major, this workgroup's scratch slot), then the pairwise routine.
+__global__ __launch_bounds__(256)
+void bwd_fallback_kernel(P p) {
+    __shared__ float smem[kBodyFloats];
+    const int n_bad = p.bad[0];
+    const int tid = threadIdx.x;
+    float *Ss = p.slot + (size_t)blockIdx.x * 2 * kD * kD, *Gs = Ss + kD * kD;
+    const int nsub = 2 * p.nck;
+    for (int i = blockIdx.x; i < n_bad; i += gridDim.x) {
+        const int ent = p.bad[1 + i];
+        const int bh = ent / nsub, sub = ent % nsub, c = sub >> 1, half = sub & 1;
+        const int seg = c / p.seg_ck;
+        const size_t ck = (size_t)bh * p.nck + c, sb = (size_t)bh * p.nseg + seg;
+        const size_t xbase = (size_t)bh * p.T * kD;
+        const int ts = c * kCk + (half ? 0 : kSub);  // the other half of the interval
+        const int Ls = min(kSub, p.T - ts);
+        float *lam = smem, *mu = lam + kBC * kBD, *X = mu + kBC * kBD, *Y = X + kBC * kBD;
+        chunk_gates<bf16_t>(p.g, p.th, xbase, ts, Ls, kD, lam, mu);
+        for (int e = tid; e < kSub * kD; e += 256) {
+            const int t = e >> 7, rc = e & 127;
+            float x = 0.f, y = 0.f;
+            if (t < Ls) {
+                const size_t xi = xbase + (size_t)(ts + t) * kD + rc;
+                if (half) {
+                    x = bf2f(p.k[xi]) * __expf(lam[(kBC - 1) * kBD + rc] - lam[t * kBD + rc] + mu[t * kBD + rc]);
+                    y = bf2f(p.v[xi]);
+                } else {
+                    x = bf2f(p.q[xi]) * __expf(lam[t * kBD + rc]);
+                    y = bf2f(p.dO[xi]);
+                }
+            }
+            X[e] = x;
+            Y[e] = y;
+        }
+        __syncthreads();
+        const int n = tid & 127;
+        for (int rr = tid >> 7; rr < kD; rr += 2) {
+            const int fi = frag_index(rr, n);
+            float s = bf2f(p.ckS[ck * kFrag + fi]);
+            if (seg > 0) s = fmaf(p.sigS[ck * kD + rr], bf2f(p.fixS[sb * kFrag + fi]), s);
+            float gg = bf2f(p.ckG[ck * kFrag + fi]);
+            if (seg < p.nseg - 1) gg = fmaf(p.sigG[ck * kD + rr], bf2f(p.fixG[sb * kFrag + fi]), gg);
+            float acc = 0.f;
+            for (int t = 0; t < Ls; ++t) acc = fmaf(X[t * kD + rr], Y[t * kD + n], acc);
+            const float d = __expf(lam[(kBC - 1) * kBD + rr]);
+            if (half) s = fmaf(d, s, acc);
+            else gg = fmaf(d, gg, acc);
+            Ss[rr * kD + n] = s;
+            Gs[rr * kD + n] = gg;
+        }
+        __syncthreads();
+        chunk_grads_body<bf16_t>(p.q, p.k, p.v, p.g, p.th, p.dO, Ss, Gs, p.dq, p.dk, p.dv, p.dg, p.dth, p.T, kD,
+                                 kD, bh, sub, smem);
+        __syncthreads();
+    }
+}
+
+// --------------------------------------------------------------- planning
+struct Plan {
+    int nck, nseg, seg_ck;
+    size_t o_ckS, o_ckG, o_ckGT, o_sigS, o_sigG, o_segS, o_segG, o_segDS, o_segDG, o_fixS, o_fixG, o_fixGT,
+        o_bad, o_slot, bytes;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan plan(long long BH, int T) {
+    Plan q{};
+    q.nck = (T + kCk - 1) / kCk;
+    // state passes: two roles x BH x nseg workgroups, about two per CU
+    long long nseg = (kCUs + BH - 1) / BH;
+    if (nseg > q.nck) nseg = q.nck;
+    if (nseg < 1) nseg = 1;
+    q.seg_ck = (int)((q.nck + nseg - 1) / nseg);
+    q.nseg = (q.nck + q.seg_ck - 1) / q.seg_ck;
+    const size_t F = (size_t)kFrag * 2, nck = (size_t)BH * q.nck, nsg = (size_t)BH * q.nseg;
+    size_t o = 0;
+    q.o_ckS = o; o += up256(nck * F);
+    q.o_ckG = o; o += up256(nck * F);
+    q.o_ckGT = o; o += up256(nck * F);
+    q.o_sigS = o; o += up256(nck * kD * 4);
+    q.o_sigG = o; o += up256(nck * kD * 4);
+    q.o_segS = o; o += up256(nsg * kD * kD * 4);
+    q.o_segG = o; o += up256(nsg * kD * kD * 4);
+    q.o_segDS = o; o += up256(nsg * kD * 4);
+    q.o_segDG = o; o += up256(nsg * kD * 4);
+    q.o_fixS = o; o += up256(nsg * F);
+    q.o_fixG = o; o += up256(nsg * F);
+    q.o_fixGT = o; o += up256(nsg * F);
+    q.o_bad = o; o += up256((1 + 2 * nck) * 4);
+    q.o_slot = o; o += (size_t)kSlowWG * 2 * kD * kD * 4;
+    q.bytes = o;
+    return q;
+}
+
+}  // namespace
+
+bool scan_bwd_mfma_supported(int T, int dk, int dv, int dtype) {
+    return dtype == 1 && dk == kD && dv == kD && T < kMaxT;
+}
+
+size_t scan_bwd_mfma_workspace(int B, int H, int T) {
+    if (B <= 0 || H <= 0 || T <= 0) return 0;
+    return plan((long long)B * H, T).bytes;
+}
+
+void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
+    const int BH = a.B * a.H;
+    const Plan q = plan(BH, a.T);
+    char *ws = reinterpret_cast<char *>(a.workspace);
+    P p;
+    p.q = (const bf16_t *)a.q; p.k = (const bf16_t *)a.k; p.v = (const bf16_t *)a.v;
+    p.g = (const bf16_t *)a.g; p.th = (const bf16_t *)a.tau; p.dO = (const bf16_t *)a.dO;
+    p.S0 = a.S0; p.dST = a.dS_T;
+    p.dq = a.dq; p.dk = a.dk_; p.dv = a.dv_; p.dg = a.dg; p.dth = a.dtau; p.dS0 = a.dS0;
+    p.ckS = (bf16_t *)(ws + q.o_ckS); p.ckG = (bf16_t *)(ws + q.o_ckG); p.ckGT = (bf16_t *)(ws + q.o_ckGT);
+    p.sigS = (float *)(ws + q.o_sigS); p.sigG = (float *)(ws + q.o_sigG);
+    p.segS = (float *)(ws + q.o_segS); p.segG = (float *)(ws + q.o_segG);
+    p.segDS = (float *)(ws + q.o_segDS); p.segDG = (float *)(ws + q.o_segDG);
+    p.fixS = (bf16_t *)(ws + q.o_fixS); p.fixG = (bf16_t *)(ws + q.o_fixG); p.fixGT = (bf16_t *)(ws + q.o_fixGT);
+    p.bad = (int *)(ws + q.o_bad);
+    p.slot = (float *)(ws + q.o_slot);
+    p.BH = BH; p.T = a.T; p.nck = q.nck; p.nseg = q.nseg; p.seg_ck = q.seg_ck;
+    hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(2 * BH * q.nseg)), dim3(256), 0, st, p);
+    if (q.nseg > 1) {
+        const size_t n = (size_t)BH * kD * kD;
+        hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    }
+    const size_t npair = (size_t)BH * q.nck;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)((npair + 7) / 8 * 16)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_fallback_kernel, dim3(kSlowWG), dim3(256), 0, st, p);
+}
+
+}  // namespace rodimus

@@ -107,8 +107,8 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
  * Backward of rodimus_scan_prefill: the gradients of
  *     L = sum(dO * o) + sum(dS_T * S_T)
  * with respect to q, k, v, g, tau and S0, for the same recurrence and gate map
- * (reverse-mode through the chunkwise form, chunks of 32 tokens; fp32
- * arithmetic).  Inputs as for rodimus_scan_prefill, plus
+ * (reverse-mode through the chunkwise form that the CodeFuse article's Rodimus
+ * block paragraph trains with).  Inputs as for rodimus_scan_prefill, plus
  *   dO   : [B, H, T, dv] in the input dtype
  *   dS_T : [B, H, dk, dv] fp32, or NULL (no gradient of the final state)
  * Outputs, all fp32 and caller-allocated:
@@ -116,9 +116,17 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
  *   grad_S0 : [B, H, dk, dv], or NULL (not returned)
  * S0 NULL means zeros, as in the forward.  Supported: fp32 or bf16 inputs,
  * dk and dv multiples of 16 up to 128 (else RODIMUS_ERR_INVALID_ARG).
- * `workspace` (state checkpoints and state gradients, 2*B*H*ceil(T/32)*dk*dv
- * fp32) must hold rodimus_scan_backward_workspace_bytes(...) bytes, else
- * RODIMUS_ERR_INVALID_ARG.  T = 0 copies dS_T (or zeros) into grad_S0.
+ * Two paths, chosen from the arguments:
+ *   - bf16 with dk = dv = 128: matrix cores (bf16 operands, fp32
+ *     accumulation, bf16 state checkpoints every 64 tokens); same accuracy
+ *     class as the bf16 forward;
+ *   - otherwise: fp32 vector arithmetic over 32-token chunks with fp32
+ *     checkpoints (workspace 2*B*H*ceil(T/32)*dk*dv fp32).
+ * `workspace` must hold rodimus_scan_backward_workspace_bytes(...) bytes, else
+ * RODIMUS_ERR_INVALID_ARG; its contents are overwritten (on the matrix-core
+ * path: about 96 KiB per (b,h) per 64 tokens, plus per-segment edges and a
+ * fixed 32 MiB).  T = 0 copies dS_T (or zeros) into grad_S0.  Calls that
+ * share one workspace must not overlap.
  */
 size_t rodimus_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
 int rodimus_scan_backward(const void *q, const void *k, const void *v, const void *g,

@@ -183,13 +183,30 @@ def test_scan_backward_rejects(kw):
     assert bwd(**kw) == rd.ERR_INVALID_ARG
 
 
+def _mfma_bwd_workspace(B, H, T):
+    """Workspace of the matrix-core backward (bf16, dk = dv = 128): bf16
+    checkpoints every 64 tokens (S, G, G^T: 32 KiB each), per-checkpoint decay
+    factors, per-segment edges, the fallback list and 256 scratch pairs."""
+    up = lambda x: (x + 255) // 256 * 256
+    BH = B * H
+    nck = -(-T // 64)
+    nseg = max(1, min(nck, -(-256 // BH)))
+    seg_ck = -(-nck // nseg)
+    nseg = -(-nck // seg_ck)
+    return (3 * up(BH * nck * 32768) + 2 * up(BH * nck * 512) + 2 * up(BH * nseg * 65536)
+            + 2 * up(BH * nseg * 512) + 3 * up(BH * nseg * 32768) + up(4 * (1 + 2 * BH * nck))
+            + 256 * 2 * 128 * 128 * 4)
+
+
 def test_scan_backward_empty_and_workspace():
     assert bwd(B=0, q=None, ws=None) == rd.OK
     assert bwd(H=0, dq=None, ws=None) == rd.OK
     assert bwd(T=0, dS0=None, q=None, ws=None) == rd.OK     # nothing requested
-    # two fp32 [dk,dv] states per (batch, head, 32-token chunk): forward checkpoints
-    # and reverse-carried state gradients
+    # generic path: two fp32 [dk,dv] states per (batch, head, 32-token chunk)
     assert rd.rodimus_scan_backward_workspace_bytes(1, 2, 40, 16, 32) == 2 * 2 * 2 * 16 * 32 * 4
-    assert rd.rodimus_scan_backward_workspace_bytes(4, 16, 4096, 128, 128) == 2 * 64 * 128 * 128 * 128 * 4
+    assert rd.rodimus_scan_backward_workspace_bytes(4, 16, 4096, 128, 128, rd.F32) == 2 * 64 * 128 * 128 * 128 * 4
+    # matrix-core path (bf16, dk = dv = 128)
+    for B, H, T in ((4, 16, 4096), (1, 16, 131072), (1, 1, 1), (3, 5, 100), (300, 1, 640)):
+        assert rd.rodimus_scan_backward_workspace_bytes(B, H, T, 128, 128) == _mfma_bwd_workspace(B, H, T)
     assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 0, 128, 128) == 0
     assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 64, 8, 128) == 0   # invalid dk
