@@ -571,12 +571,6 @@ void bwd_grad_kernel(P p) {
         aI = mfma(opPT[ks], trf(kOffKT, rr, ks), aI);
         kI = mfma(opP[ks], trf(kOffQT, rr, ks), kI);
     }
-    // the epilogue's inputs again (L2-resident)
-    uint4 Eq[2], Ek[2], Eg[2], Eth[2];
-    load_one<2>(Eq, rq, t0, r, cg);
-    load_one<2>(Ek, rk, t0, r, cg);
-    load_one<2>(Eg, rg, t0, r, cg);
-    load_one<2>(Eth, rth, t0, r, cg);
     __syncthreads();  // operand rows are dead: stage the accumulators
     float *sQI = reinterpret_cast<float *>(smem), *sQ1 = sQI + kSub * kSR, *sKI = sQ1 + kSub * kSR,
           *sX2 = sKI + kSub * kSR;
@@ -589,6 +583,10 @@ void bwd_grad_kernel(P p) {
         sX2[t * kSR + rr] = ax[i];
     }
     if (h == 0) sDec[rr] = dec;
+    // the epilogue's inputs again (L2-resident), once the accumulators are free
+    uint4 Eq[2], Ek[2], Eg[2], Eth[2];
+    load_one<2>(Eg, rg, t0, r, cg);
+    load_one<2>(Eth, rth, t0, r, cg);
     __syncthreads();
 
     // ---- epilogue, producer layout: tokens 2r, 2r+1, channels 8cg..8cg+7 ----
@@ -596,6 +594,9 @@ void bwd_grad_kernel(P p) {
     // products, so that their reverse cumulative sum telescopes exactly.
     float l2a[2][8], l2b[2][8], lend[8];
     gates_scan_gt<kSub>(Eg, Eth, t0, p.T, r, l, l2a, l2b, lend);
+    __builtin_amdgcn_sched_barrier(0);
+    load_one<2>(Eq, rq, t0, r, cg);
+    load_one<2>(Ek, rk, t0, r, cg);
     float dlam[2][8], dmu[2][8], ebs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ebs[e] = 0.f;
@@ -632,6 +633,7 @@ void bwd_grad_kernel(P p) {
             *reinterpret_cast<float4 *>(ok) = make_float4(dkv[0], dkv[1], dkv[2], dkv[3]);
             *reinterpret_cast<float4 *>(ok + 4) = make_float4(dkv[4], dkv[5], dkv[6], dkv[7]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one token at a time (register pressure)
     }
     float dl[2][8];
 #pragma unroll
@@ -661,7 +663,12 @@ void bwd_grad_kernel(P p) {
         unpack8(Eg[tt], gf);
         unpack8(Eth[tt], tf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ddts_gate_grads(gf[e], tf[e], dl[tt][e], dmu[tt][e], dgv[e], dtv[e]);
+        for (int e = 0; e < 8; ++e) {
+            // recompute the gate exponentials here rather than keep the
+            // epilogue's first ones alive (register pressure)
+            asm volatile("" : "+v"(gf[e]), "+v"(tf[e]));
+            ddts_gate_grads(gf[e], tf[e], dl[tt][e], dmu[tt][e], dgv[e], dtv[e]);
+        }
         float *og = p.dg + (rowbase + t0 + t) * kD + 8 * cg, *ot = p.dth + (rowbase + t0 + t) * kD + 8 * cg;
         *reinterpret_cast<float4 *>(og) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
         *reinterpret_cast<float4 *>(og + 4) = make_float4(dgv[4], dgv[5], dgv[6], dgv[7]);
