@@ -1,7 +1,7 @@
 """Benchmark of the Rodimus* token-mixer hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--only all|prefill|decode|long|swska|swska_decode|backward|copy]
+                    [--only all|prefill|decode|long|swska|swska_decode|backward|varlen|copy]
 
 A step is one rodimus_scan_prefill call over the 1.6B-shaped prefill batch
 (B=4, T=4096, H=16, dk=dv=128, bf16 inputs, fp32 state, C=64) with every input
@@ -10,7 +10,8 @@ decode state update (256 sequences x 16 heads, fp32 128x128 states, in-place
 steps cycling over 8 resident input sets) is timed in the same run and
 reported as HBM GB/s and fraction of peak, as the metric asks.  The
 long-context prefill (T=131072), SW-SKA (T=32768, w=4096), the SW-SKA decode
-step and the backward of the prefill scan (same 1.6B batch) are timed as
+step, the backward of the prefill scan (same 1.6B batch) and a packed
+dynamic batch of 64 ragged requests (16384 tokens per head) are timed as
 extras.
 
 Timing: W untimed warm-up steps, then K steps between two HIP events on the
@@ -167,6 +168,33 @@ def bench_prefill(cfg, steps, warmup):
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
                 gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
                 workspace_bytes=nws)
+
+
+def bench_varlen(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    N, H, total, dk, dv, C = cfg["N"], cfg["H"], cfg["total"], cfg["dk"], cfg["dv"], cfg["chunk"]
+    L = workloads.ragged_lengths(cfg["seed"], N, total, cfg["min_len"])
+    x = workloads.packed_scan_inputs(cfg["seed"], H, total, dk, dv, cfg["dtype"])
+    d = {n: _dev(x[n]) for n in NAMES}
+    del x
+    cu = torch.from_numpy(workloads.cu_seqlens(L)).cuda()
+    maxlen = int(L.max())
+    o = torch.empty(H, total, dv, dtype=d["q"].dtype, device="cuda")
+    ST = torch.empty(N, H, dk, dv, dtype=torch.float32, device="cuda")
+    nws = rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, maxlen, dk, dv, C, rd.BF16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rd.rodimus_scan_prefill_varlen(d["q"], d["k"], d["v"], d["g"], d["theta"], cu, maxlen, None, C, o=o,
+                                       S_T=ST, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    # per token-head q, k, g, tau, v in and o out (bf16), plus every fp32 S_T
+    nbytes = H * total * (4 * dk * 2 + dv * 2 + dv * 2) + N * H * dk * dv * 4
+    return dict(ms=ms, tokens_per_s=total / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                sequences=N, max_len=maxlen, min_len=int(L.min()))
 
 
 def backward_bytes(B, H, T, dk, dv):
@@ -387,7 +415,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "backward", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "backward", "varlen",
+                             "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -413,6 +442,8 @@ def main():
             r = bench_swska_decode(workloads.CONFIGS["swska_decode_N64_w4096"], args.steps, args.warmup)
         elif args.only == "backward":
             r = bench_backward(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup)
+        elif args.only == "varlen":
+            r = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
         else:
             r = bench_copy()
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
@@ -434,6 +465,8 @@ def main():
     sd = bench_swska_decode(sdc, sdc["steps"], 10)
     print("bench: backward_1p6b_T4096", file=sys.stderr, flush=True)
     bw = bench_backward(cfg, max(5, args.steps // 2), 2)
+    print("bench: prefill_varlen_N64_16K", file=sys.stderr, flush=True)
+    vl = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu:
@@ -498,6 +531,12 @@ def main():
                              "kernel": "rodimus_scan_backward call (state passes + combine + "
                              "gradients + fallback)", "algorithmic_bytes": bw["bytes"],
                              "workspace_bytes": bw["workspace_bytes"]}},
+            "prefill_varlen_N64_16K": {
+                "ms": round(vl["ms"], 4), "tokens_per_s": round(vl["tokens_per_s"]),
+                "sequences": vl["sequences"], "min_len": vl["min_len"], "max_len": vl["max_len"],
+                "roofline": {"bound": "hbm", "achieved": round(vl["gbs"], 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(vl["gbs"] / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": vl["bytes"]}},
         },
     }
     print(json.dumps(line), flush=True)

@@ -37,6 +37,7 @@ LIB_PATH = os.path.join(_HERE, "librodimus.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 F32, BF16 = 0, 1
 EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill",
+            "rodimus_scan_prefill_varlen_workspace_bytes", "rodimus_scan_prefill_varlen",
             "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward", "rodimus_decode_step",
             "sw_ska_attn", "sw_ska_decode_workspace_bytes", "sw_ska_decode_step",
             "rodimus_status_string")
@@ -63,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.rodimus_scan_prefill_workspace_bytes.restype = sz
         L.rodimus_scan_prefill.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
         L.rodimus_scan_prefill.restype = i
+        L.rodimus_scan_prefill_varlen_workspace_bytes.argtypes = [i] * 7
+        L.rodimus_scan_prefill_varlen_workspace_bytes.restype = sz
+        L.rodimus_scan_prefill_varlen.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
+        L.rodimus_scan_prefill_varlen.restype = i
         L.rodimus_scan_backward_workspace_bytes.argtypes = [i] * 6
         L.rodimus_scan_backward_workspace_bytes.restype = sz
         L.rodimus_scan_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
@@ -155,6 +160,52 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
                                     _ptr(o), _ptr(S_T), B, H, T, dk, dv, chunk, dt,
                                     _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "rodimus_scan_prefill")
+    return o, S_T
+
+
+def rodimus_scan_prefill_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, chunk=64, dtype=BF16) -> int:
+    return int(lib().rodimus_scan_prefill_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, chunk, dtype))
+
+
+def rodimus_scan_prefill_varlen(q, k, v, g, tau, cu_seqlens, max_seqlen: int, S0=None, chunk: int = 64, *,
+                                o=None, S_T=None, want_state: bool = True, workspace=None,
+                                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed ragged batch.  q, k, g, tau: [H,total,dk]; v: [H,total,dv];
+    cu_seqlens: int32 [N+1] on the device (sequence s = rows cu[s]..cu[s+1]-1);
+    max_seqlen >= every length; S0: [N,H,dk,dv] float32 or None.
+    Returns (o [H,total,dv], S_T [N,H,dk,dv] float32 or None)."""
+    H, total, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs N + 1 >= 1 entries")
+    for x in (k, g, tau, v):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau must share one dtype")
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (H, total, dk), nm)
+    _shape(v, (H, total, dv), "v")
+    _shape(S0, (N, H, dk, dv), "S0")
+    _shape(o, (H, total, dv), "o")
+    _shape(S_T, (N, H, dk, dv), "S_T")
+    for x, nm in ((S0, "S0"), (S_T, "S_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    if o is None:
+        o = torch.empty((H, total, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = rodimus_scan_prefill_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, chunk, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rodimus_scan_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S0),
+                                           _ptr(o), _ptr(S_T), _ptr(cu_seqlens), N, H, total, max_seqlen,
+                                           dk, dv, chunk, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "rodimus_scan_prefill_varlen")
     return o, S_T
 
 

@@ -95,6 +95,46 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
     return hip_status();
 }
 
+size_t rodimus_scan_prefill_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,
+                                                   int chunk, int dtype) {
+    return rodimus_scan_prefill_workspace_bytes(N, H, max_seqlen, dk, dv, chunk, dtype);
+}
+
+int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, const void *g,
+                                const void *tau, const float *S0, void *o, float *S_T,
+                                const int *cu_seqlens, int N, int H, int total_T, int max_seqlen,
+                                int dk, int dv, int chunk, int dtype, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (!scan_sizes_ok(N, H, max_seqlen, dk, dv, chunk, dtype) || total_T < 0)
+        return RODIMUS_ERR_INVALID_ARG;
+    if ((long long)H * total_T * (dk > dv ? dk : dv) > (1LL << 46)) return RODIMUS_ERR_INVALID_ARG;
+    if (!ok_opt_ptr(S0) || !ok_opt_ptr(S_T) || !ok_opt_ptr(workspace)) return RODIMUS_ERR_INVALID_ARG;
+    if (S0 && S_T && S0 == S_T) return RODIMUS_ERR_INVALID_ARG;
+    if (chunk == 0) chunk = 64;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0 || H == 0) return RODIMUS_OK;
+    if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3) != 0) return RODIMUS_ERR_INVALID_ARG;
+    if (max_seqlen == 0 || total_T == 0) {  // every sequence is empty
+        if (S_T) {
+            launch_state_copy(S0, S_T, (size_t)N * H * dk * dv, st);
+            return hip_status();
+        }
+        return RODIMUS_OK;
+    }
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(o))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanPlan plan = plan_scan(N, H, max_seqlen, dk, dv, chunk, dtype);
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanArgs a{q, k, v, g, tau, S0, o, S_T, N, H, max_seqlen, dk, dv, chunk, dtype, workspace,
+               workspace_bytes};
+    a.cu = cu_seqlens;
+    a.total = total_T;
+    if (plan.mfma) launch_scan_mfma(a, plan, st);
+    else launch_scan_generic(a, st);
+    return hip_status();
+}
+
 size_t rodimus_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
     if (!scan_sizes_ok(B, H, T, dk, dv, 0, dtype)) return 0;
     if (scan_bwd_mfma_supported(T, dk, dv, dtype)) return scan_bwd_mfma_workspace(B, H, T);

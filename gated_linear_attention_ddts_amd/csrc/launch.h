@@ -13,6 +13,10 @@ struct ScanArgs {
     int B, H, T, dk, dv, chunk, dtype;
     void *workspace;
     size_t workspace_bytes;
+    // packed variable-length batch (nullable): B sequences, sequence s in rows
+    // cu[s] .. cu[s+1]-1 of each head's [total][d] rows, T = longest length
+    const int *cu = nullptr;
+    int total = 0;
 };
 
 struct ScanBwdArgs {

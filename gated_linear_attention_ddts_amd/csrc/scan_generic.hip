@@ -31,7 +31,7 @@ void scan_generic_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k,
                          const Tin *__restrict__ v, const Tin *__restrict__ g,
                          const Tin *__restrict__ th, const float *__restrict__ S0,
                          Tin *__restrict__ o, float *__restrict__ S_T,
-                         int T, int dv, int C) {
+                         int Tmax, int dv, int C, const int *__restrict__ cu, int H, int total) {
     __shared__ float bufQ[kGenMaxC * DK];       // log2 a, then Lam, then Qt
     __shared__ float bufK[kGenMaxC * DK];       // log2 beta, then Kh, then Kb
     __shared__ float bufV[kGenMaxC * kGenCols];  // v tile (this block's columns)
@@ -43,8 +43,18 @@ void scan_generic_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k,
     const int tid = threadIdx.x;
     const int j = blockIdx.y * kGenCols + tid;
     const bool active = j < dv;
-    const size_t xbase = (size_t)bh * T * DK;
-    const size_t vbase = (size_t)bh * T * dv;
+    // rows of (b,h): batched [B][H][T], or a packed sequence (bh = s * H + h,
+    // rows cu[s] .. cu[s+1]-1 of head h, clamped to [0, total] and Tmax)
+    size_t row0 = (size_t)bh * Tmax;
+    int T = Tmax;
+    if (cu) {
+        const int s = bh / H, h = bh - s * H;
+        const int a = min(max(cu[s], 0), total), b = min(max(cu[s + 1], a), total);
+        row0 = (size_t)h * total + a;
+        T = min(b - a, Tmax);
+    }
+    const size_t xbase = row0 * DK;
+    const size_t vbase = row0 * dv;
 
     float S[DK];
 #pragma unroll
@@ -154,7 +164,8 @@ static void launch_dk(const ScanArgs &a, hipStream_t st) {
     dim3 grid(a.B * a.H, (a.dv + kGenCols - 1) / kGenCols);
     hipLaunchKernelGGL((scan_generic_kernel<Tin, DK>), grid, dim3(64), 0, st,
                        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.g,
-                       (const Tin *)a.tau, a.S0, (Tin *)a.o, a.S_T, a.T, a.dv, a.chunk);
+                       (const Tin *)a.tau, a.S0, (Tin *)a.o, a.S_T, a.T, a.dv, a.chunk, a.cu, a.H,
+                       a.total);
 }
 
 template <typename Tin>

@@ -79,10 +79,32 @@ struct Params {
     float *wsS;       // [(G-1)*P][BH][128][128] sub-segment states / incoming states
     float *wsA;       // [(G-1)*P][BH][128] total log2 decay of each sub-segment
     int BH, T, G, seg_len, P, sub_len;
+    // packed variable-length batch: sequence s = bh / H occupies rows
+    // cu[s] .. cu[s+1]-1 of head h = bh % H's [total][128] rows; T is then the
+    // longest length (the segment plan)
+    const int *cu;
+    int H, total;
 };
 
+// Rows of (b,h): first row and length.  The packed form clamps each span to
+// [0, total] and to T, so a malformed offset table cannot address memory
+// outside the inputs and outputs.
+template <bool VL>
+__device__ __forceinline__ void seq_span(const Params &p, int bh, size_t &rowbase, int &len) {
+    if (!VL) {
+        rowbase = (size_t)bh * p.T;
+        len = p.T;
+        return;
+    }
+    const int s = bh / p.H, h = bh - s * p.H;
+    const int a = min(max(uni(p.cu[s]), 0), p.total);
+    const int b = min(max(uni(p.cu[s + 1]), a), p.total);
+    rowbase = (size_t)h * p.total + a;
+    len = min(b - a, p.T);
+}
+
 // ------------------------------------------------------------- phase 3 (full)
-template <int C>
+template <int C, bool VL>
 __global__ __launch_bounds__(512, 1)
 void scan_full_kernel(Params p) {
     constexpr int TPR = C / 16, NT = C / 32;
@@ -94,10 +116,12 @@ void scan_full_kernel(Params p) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
     const int bh = uni(blockIdx.x % p.BH), seg = uni(blockIdx.x / p.BH);
     if (seg >= p.G) return;
+    size_t rowbase;
+    int Tb;
+    seq_span<VL>(p, bh, rowbase, Tb);
     const int t_begin = seg * p.seg_len;
-    const int t_end = min(p.T, t_begin + p.seg_len);
-    const int nch = (t_end - t_begin + C - 1) / C;
-    const size_t rowbase = (size_t)bh * p.T;
+    const int t_end = min(Tb, t_begin + p.seg_len);
+    const int nch = max(0, (t_end - t_begin + C - 1) / C);
 
     if (tid < 4) sFlag[tid] = 0;
     __syncthreads();
@@ -106,9 +130,9 @@ void scan_full_kernel(Params p) {
         // ======================= producers =======================
         const int r = l & 15, cg = (w << 2) | (l >> 4);
         Rsrc rs;
-        rs.q = rsrc(p.q + rowbase * kD, p.T); rs.k = rsrc(p.k + rowbase * kD, p.T);
-        rs.v = rsrc(p.v + rowbase * kD, p.T); rs.g = rsrc(p.g + rowbase * kD, p.T);
-        rs.th = rsrc(p.th + rowbase * kD, p.T);
+        rs.q = rsrc(p.q + rowbase * kD, Tb); rs.k = rsrc(p.k + rowbase * kD, Tb);
+        rs.v = rsrc(p.v + rowbase * kD, Tb); rs.g = rsrc(p.g + rowbase * kD, Tb);
+        rs.th = rsrc(p.th + rowbase * kD, Tb);
         Raw<C, true> R;
         load_raw<C, true>(R, rs, t_begin, r, cg);
         for (int kk = 0; kk <= nch; ++kk) {
@@ -372,6 +396,7 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false> &R, const Rsrc 
     __syncthreads();
 }
 
+template <bool VL>
 __global__ __launch_bounds__(256, 2)
 void scan_state_kernel(Params p) {
     constexpr int CS = 32, TPR = CS / 16;
@@ -386,13 +411,16 @@ void scan_state_kernel(Params p) {
     const int seg_begin = seg * p.seg_len;
     const int t_begin = seg_begin + part * p.sub_len;
     const int t_end = min(seg_begin + p.seg_len, t_begin + p.sub_len);  // whole chunks
-    const int nch = (t_end - t_begin) / CS;
-    const size_t rowbase = (size_t)bh * p.T;
+    size_t rowbase;
+    int Tb;
+    seq_span<VL>(p, bh, rowbase, Tb);
+    // chunks of this sub-segment that hold tokens (all of them unless packed)
+    const int nch = VL ? max(0, min((t_end - t_begin) / CS, (Tb - t_begin + CS - 1) / CS)) : (t_end - t_begin) / CS;
     const int r = l & 15, cg = (w << 2) | (l >> 4);
 
     Rsrc rs;
-    rs.k = rsrc(p.k + rowbase * kD, p.T); rs.v = rsrc(p.v + rowbase * kD, p.T);
-    rs.g = rsrc(p.g + rowbase * kD, p.T); rs.th = rsrc(p.th + rowbase * kD, p.T);
+    rs.k = rsrc(p.k + rowbase * kD, Tb); rs.v = rsrc(p.v + rowbase * kD, Tb);
+    rs.g = rsrc(p.g + rowbase * kD, Tb); rs.th = rsrc(p.th + rowbase * kD, Tb);
     rs.q = rs.k;
 
     f32x16_t S[4];
@@ -405,14 +433,14 @@ void scan_state_kernel(Params p) {
     // chunks are visited last to first; two chunks of raw inputs are in flight
     Raw<CS, false> Ra, Rb;
     const int c0 = nch - 1;
-    load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
+    if (c0 >= 0) load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
     if (c0 >= 1) load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
     for (int c = c0; c >= 0; c -= 2) {
         state_chunk<TPR>(Ra, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1, sKbT, sVT,
-                         S, rho, r, cg, l, w, h, l32, p.T);
+                         S, rho, r, cg, l, w, h, l32, Tb);
         if (c >= 1)
             state_chunk<TPR>(Rb, rs, t_begin + (c - 1) * CS, c >= 3 ? t_begin + (c - 3) * CS : -1,
-                             sKbT, sVT, S, rho, r, cg, l, w, h, l32, p.T);
+                             sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
     }
     float *So = p.wsS + ((size_t)sub * p.BH + bh) * kD * kD;
 #pragma unroll
@@ -521,14 +549,23 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.wsA = p.wsS ? p.wsS + (size_t)nsub * BH * kD * kD : nullptr;
     p.BH = BH; p.T = a.T; p.G = q.G; p.seg_len = q.per_seg * a.chunk; p.P = q.P;
     p.sub_len = q.sub * a.chunk;
+    p.cu = a.cu; p.H = a.H; p.total = a.total;
+    const bool vl = a.cu != nullptr;
     if (q.G > 1) {
-        hipLaunchKernelGGL(scan_state_kernel, dim3(nsub * BH), dim3(256), 0, st, p);
+        if (vl) hipLaunchKernelGGL(scan_state_kernel<true>, dim3(nsub * BH), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(scan_state_kernel<false>, dim3(nsub * BH), dim3(256), 0, st, p);
         const size_t n4 = (size_t)BH * kD * kD / 4;
         hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                            a.S0, p.wsS, p.wsA, BH, nsub, q.P);
     }
-    if (a.chunk == 64) hipLaunchKernelGGL((scan_full_kernel<64>), dim3(q.G * BH), dim3(512), 0, st, p);
-    else hipLaunchKernelGGL((scan_full_kernel<32>), dim3(q.G * BH), dim3(512), 0, st, p);
+    const dim3 grid(q.G * BH), blk(512);
+    if (a.chunk == 64) {
+        if (vl) hipLaunchKernelGGL((scan_full_kernel<64, true>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((scan_full_kernel<64, false>), grid, blk, 0, st, p);
+    } else {
+        if (vl) hipLaunchKernelGGL((scan_full_kernel<32, true>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((scan_full_kernel<32, false>), grid, blk, 0, st, p);
+    }
 }
 
 }  // namespace rodimus

@@ -6,7 +6,8 @@
  * hand-written HIP kernels launched asynchronously on the caller's stream:
  *
  *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
- *                        whole prompt, in chunkwise-parallel form;
+ *                        whole prompt, in chunkwise-parallel form (also over
+ *                        a packed batch of ragged sequences, _varlen);
  *  rodimus_scan_backward its gradients with respect to every input;
  *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
  *  sw_ska_attn           sliding-window attention with one key matrix shared
@@ -102,6 +103,39 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
                          const void *tau, const float *S0, void *o, float *S_T,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rodimus_scan_prefill over a packed batch of sequences of different lengths
+ * (dynamic batching of short requests, each with its own small fixed-size
+ * state: the Tupoi O(1)-memory practice guide, pwwt.cn/news/4131393,
+ * section 4.2 on batching and resource management).  Per head, the N
+ * sequences are concatenated:
+ *
+ *   q, k, g, tau : [H, total_T, dk]     v, o : [H, total_T, dv]   (dtype)
+ *   cu_seqlens   : int32 [N + 1], device; sequence s occupies rows
+ *                  cu_seqlens[s] .. cu_seqlens[s+1]-1 of every head
+ *                  (non-decreasing, cu_seqlens[0] = 0, cu_seqlens[N] = total_T)
+ *   S0, S_T      : [N, H, dk, dv] float, optional as in rodimus_scan_prefill
+ *   max_seqlen   : at least the longest sequence; it sizes the segment plan
+ *                  and the workspace (query with the _workspace_bytes call)
+ *
+ * Each sequence gives exactly what rodimus_scan_prefill gives for it alone
+ * (same arithmetic; bitwise equal to a batched call of equal-length
+ * sequences).  The table is read on the device only: the kernels clamp each
+ * span to [0, total_T] and to max_seqlen, so a malformed table yields wrong
+ * values but no access outside the tensors; rows of o that no span covers
+ * are left untouched.  Sizes: N, H, total_T, max_seqlen >= 0; cu_seqlens
+ * 4-byte aligned and non-NULL when N, H > 0; other rules as for
+ * rodimus_scan_prefill.  max_seqlen = 0 or total_T = 0 copies S0 (or zeros)
+ * to S_T.
+ */
+size_t rodimus_scan_prefill_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,
+                                                   int chunk, int dtype);
+int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, const void *g,
+                                const void *tau, const float *S0, void *o, float *S_T,
+                                const int *cu_seqlens, int N, int H, int total_T, int max_seqlen,
+                                int dk, int dv, int chunk, int dtype, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Backward of rodimus_scan_prefill: the gradients of

@@ -210,3 +210,34 @@ def test_scan_backward_empty_and_workspace():
         assert rd.rodimus_scan_backward_workspace_bytes(B, H, T, 128, 128) == _mfma_bwd_workspace(B, H, T)
     assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 0, 128, 128) == 0
     assert rd.rodimus_scan_backward_workspace_bytes(1, 1, 64, 8, 128) == 0   # invalid dk
+
+
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S0=None, o=FAKE, S_T=None, cu=FAKE, N=3, H=2,
+             total=100, maxlen=64, dk=128, dv=128, chunk=64, dtype=rd.BF16, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_prefill_varlen(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S0"], a["o"],
+                                                a["S_T"], a["cu"], a["N"], a["H"], a["total"], a["maxlen"],
+                                                a["dk"], a["dv"], a["chunk"], a["dtype"], a["ws"],
+                                                a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(o=None), dict(cu=None), dict(cu=FAKE + 2), dict(q=MISALIGNED), dict(S0=MISALIGNED),
+    dict(N=-1), dict(H=-1), dict(total=-1), dict(maxlen=-1), dict(dk=8), dict(chunk=48), dict(dtype=3),
+    dict(S0=FAKE, S_T=FAKE), dict(ws=MISALIGNED),
+])
+def test_scan_prefill_varlen_rejects(kw):
+    assert varlen(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_scan_prefill_varlen_empty_and_workspace():
+    assert varlen(N=0, q=None, cu=None) == rd.OK
+    assert varlen(H=0, o=None, cu=None) == rd.OK
+    assert varlen(maxlen=0, q=None, o=None) == rd.OK      # every sequence empty, nothing to copy
+    assert varlen(total=0, q=None, o=None) == rd.OK
+    # the segment plan of a packed batch is that of N sequences of the longest length
+    for N, H, L in ((3, 16, 4096), (64, 16, 448), (1, 1, 1)):
+        assert (rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16)
+                == rd.rodimus_scan_prefill_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16))

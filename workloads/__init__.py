@@ -131,7 +131,35 @@ def device_normal(shape, seed, mu=0.0, sigma=1.0, dtype="bf16", device="cuda"):
     return x.to(torch.bfloat16) if dtype == "bf16" else x
 
 
-# The five workloads, named by what they are.
+def ragged_lengths(seed, N, total, min_len=1, sigma=0.8):
+    """N sequence lengths that sum to `total` (each >= min_len): a seeded
+    log-normal mix of short and long requests, as a dynamic batch packs them."""
+    rng = np.random.default_rng(seed)
+    w = rng.lognormal(0.0, sigma, size=N)
+    extra = total - N * min_len
+    if extra < 0:
+        raise ValueError("total too small for N sequences of min_len")
+    raw = w / w.sum() * extra
+    L = np.floor(raw).astype(np.int64)
+    # hand the rounding remainder to the largest fractional parts
+    rem = int(extra - L.sum())
+    L[np.argsort(raw - L)[::-1][:rem]] += 1
+    return (L + min_len).astype(np.int64)
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """Offsets [0, l0, l0+l1, ...] (int32) of a packed batch."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def packed_scan_inputs(seed, H, total, dk, dv, dtype="bf16"):
+    """q, k, v, g, theta of a packed batch: [H, total, d] each, drawn as
+    scan_inputs with B = 1 (the sequences' rows are independent draws)."""
+    x = scan_inputs(seed, 1, H, total, dk, dv, dtype)
+    return {n: Tensor(t.values[0], t.dtype) for n, t in x.items()}
+
+
+# The workloads, named by what they are.
 CONFIGS = {
     "tiny_fp32_scan": dict(kind="scan", B=1, H=2, T=256, dk=16, dv=32, dtype="fp32", chunk=32,
                            gate_mu=0.0, seed=1),
@@ -147,4 +175,8 @@ CONFIGS = {
     # (shared K [64, 4096, 128], per-head V [64, 16, 4096, 128]), one token per step
     "swska_decode_N64_w4096": dict(kind="swska_decode", N=64, H=16, dk=128, dv=128, window=4096,
                                    pos0=8192, steps=200, pool=8, dtype="bf16", seed=6),
+    # a dynamic batch: 64 requests of log-normal lengths packed into 16384
+    # tokens per head (the token count of the 1.6B batch), 16 heads
+    "prefill_varlen_N64_16K": dict(kind="varlen", N=64, H=16, total=16384, min_len=16, dk=128,
+                                   dv=128, dtype="bf16", chunk=64, seed=7),
 }
