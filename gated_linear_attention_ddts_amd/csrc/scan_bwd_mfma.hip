@@ -261,14 +261,23 @@ constexpr int kOffB1 = kOffQT, kOffB2 = kOffKT;
 static_assert(4 * kSub * kSR * 4 <= kOffGam, "staging fits in the dead operand rows");
 static_assert(kGradLDS <= 80 * 1024, "two workgroups per CU");
 
-__device__ __forceinline__ void ld_frag(const bf16_t *base, int f, int l, float (&x)[8]) {
-    unpack8(*reinterpret_cast<const uint4 *>(base + ((size_t)f * 64 + l) * 8), x);
-}
 __device__ __forceinline__ bf16x8_t pack_frag(const float (&x)[8]) {
     return __builtin_bit_cast(bf16x8_t, make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]),
                                                    pack2(x[4], x[5]), pack2(x[6], x[7])));
 }
 __device__ __forceinline__ float bf_round(float x) { return lo_bf(pack2(x, 0.f)); }
+__device__ __forceinline__ uint4 ld_raw(const bf16_t *base, int f, int l) {
+    return *reinterpret_cast<const uint4 *>(base + ((size_t)f * 64 + l) * 8);
+}
+// x + sig * y for 8 packed bf16, rounded back to bf16
+__device__ __forceinline__ uint4 fix_raw(const uint4 &x, const uint4 &y, float sig) {
+    float a[8], b[8];
+    unpack8(x, a);
+    unpack8(y, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = fmaf(sig, b[e], a[e]);
+    return __builtin_bit_cast(uint4, pack_frag(a));
+}
 
 // Bridge of the first half to its checkpoint would be the identity; each
 // workgroup's own half is (c, half), the bridged one the other half of c.
@@ -365,6 +374,16 @@ void bwd_grad_kernel(P p) {
             for (int e = 0; e < 8; ++e) sGam[8 * cg + e] = lend[e];
         }
     }
+    // this interval's checkpoints, raw: all loads in flight at once, their
+    // latency overlapping the bridge operands
+    const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag, *cGT = p.ckGT + ck * kFrag;
+    uint4 rS[8], rG[8], rGT[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        rS[s] = ld_raw(cS, 8 * w + s, l);
+        rG[s] = ld_raw(cG, 8 * w + s, l);
+        rGT[s] = ld_raw(cGT, 8 * w + s, l);
+    }
     // bridge operands: first half -> Kb0^T, V0^T (the state through it);
     // second half -> Qt1^T, dO1^T (the gradient back through it)
     {
@@ -393,25 +412,46 @@ void bwd_grad_kernel(P p) {
     auto rowf = [&](int off, int row, int s) { return lds16(smem, off + (row * kQR + 16 * s + 8 * h) * 2); };
     auto trf = [&](int off, int row, int ks) { return lds16(smem, off + (row * kT32 + 16 * ks + 8 * h) * 2); };
 
-    // S entering and G (both orientations) leaving this half, bf16 operands
+    // S entering and G (both orientations) leaving this half, bf16 operands;
+    // checkpoints of later / earlier segments are completed with the segment
+    // fix-up (loaded all at once)
     bf16x8_t Sf[8], Gf[8], GTf[8];
     const float sigS = fixS ? p.sigS[ck * kD + rr] : 0.f;
     const float sigG = fixG ? sSig[rr] : 0.f;
-    const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag, *cGT = p.ckGT + ck * kFrag;
     const bf16_t *xS = p.fixS + sb * kFrag, *xG = p.fixG + sb * kFrag, *xGT = p.fixGT + sb * kFrag;
+    if (fixS) {
+        uint4 f[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) f[s] = ld_raw(xS, 8 * w + s, l);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) rS[s] = fix_raw(rS[s], f[s], sigS);
+    }
+    if (fixG) {
+        uint4 f[8], fT[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            f[s] = ld_raw(xG, 8 * w + s, l);
+            fT[s] = ld_raw(xGT, 8 * w + s, l);
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            rG[s] = fix_raw(rG[s], f[s], sigG);
+            float x[8], y[8];
+            unpack8(rGT[s], x);
+            unpack8(fT[s], y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
+            rGT[s] = __builtin_bit_cast(uint4, pack_frag(x));
+        }
+    }
     if (half) {
         // S through the first half: diag(2^{Gam0}) S_c + Kb0^T V0 (transposed accumulators)
         const float eg = exp2_fast(sGamB[rr]);
         f32x16_t A[4];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            float x[8], y[8];
-            ld_frag(cS, 8 * w + s, l, x);
-            if (fixS) {
-                ld_frag(xS, 8 * w + s, l, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigS, y[e], x[e]);
-            }
+            float x[8];
+            unpack8(rS[s], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
         }
@@ -420,24 +460,10 @@ void bwd_grad_kernel(P p) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) A[q] = mfma(trf(kOffB2, 32 * q + l32, ks), trf(kOffB1, rr, ks), A[q]);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Sf[s] = cvt8(A[s >> 1], 8 * (s & 1));
-#pragma unroll
         for (int s = 0; s < 8; ++s) {
-            float x[8], y[8];
-            ld_frag(cG, 8 * w + s, l, x);
-            if (fixG) {
-                ld_frag(xG, 8 * w + s, l, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigG, y[e], x[e]);
-            }
-            Gf[s] = pack_frag(x);
-            ld_frag(cGT, 8 * w + s, l, x);
-            if (fixG) {
-                ld_frag(xGT, 8 * w + s, l, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
-            }
-            GTf[s] = pack_frag(x);
+            Sf[s] = cvt8(A[s >> 1], 8 * (s & 1));
+            Gf[s] = __builtin_bit_cast(bf16x8_t, rG[s]);
+            GTf[s] = __builtin_bit_cast(bf16x8_t, rGT[s]);
         }
     } else {
         // G back through the second half: diag(2^{Gam1}) G_c + Qt1^T dO1, both
@@ -447,13 +473,8 @@ void bwd_grad_kernel(P p) {
             const float eg = exp2_fast(sGamB[rr]);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                float x[8], y[8];
-                ld_frag(cG, 8 * w + s, l, x);
-                if (fixG) {
-                    ld_frag(xG, 8 * w + s, l, y);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = fmaf(sigG, y[e], x[e]);
-                }
+                float x[8];
+                unpack8(rG[s], x);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
             }
@@ -468,14 +489,8 @@ void bwd_grad_kernel(P p) {
             f32x16_t B[4];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                float x[8], y[8];
-                ld_frag(cGT, 8 * w + s, l, x);
-                if (fixG) {
-                    ld_frag(xGT, 8 * w + s, l, y);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
-                }
+                float x[8];
+                unpack8(rGT[s], x);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     B[s >> 1][8 * (s & 1) + e] = x[e] * exp2_fast(sGamB[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)]);
@@ -488,16 +503,7 @@ void bwd_grad_kernel(P p) {
             for (int s = 0; s < 8; ++s) GTf[s] = cvt8(B[s >> 1], 8 * (s & 1));
         }
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            float x[8], y[8];
-            ld_frag(cS, 8 * w + s, l, x);
-            if (fixS) {
-                ld_frag(xS, 8 * w + s, l, y);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = fmaf(sigS, y[e], x[e]);
-            }
-            Sf[s] = pack_frag(x);
-        }
+        for (int s = 0; s < 8; ++s) Sf[s] = __builtin_bit_cast(bf16x8_t, rS[s]);
     }
 
     // ---- matrix-core products (wave w: output columns 32w..32w+31) ----
