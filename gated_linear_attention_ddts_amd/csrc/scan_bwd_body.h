@@ -44,7 +44,9 @@ __device__ __forceinline__ void ddts_gate_grads(float g, float th, float dla, fl
     const float dtau = xt * rt * rt;                                // sigmoid(th) sigmoid(-th)
     const float x = exp2_fast(-fabsf(g) * kLog2e);                  // e^{-|g|}
     const float u = 1.f + x, ru = __builtin_amdgcn_rcpf(u);
-    const float L = (u == 1.f) ? x : log2_fast(u) * kLn2 * (x / (u - 1.f));   // log1p(x)
+    // log1p(x) as log(u) * x / (u - 1) (exact when u == 1); the hardware
+    // reciprocal's 1-ulp error is far below the gradients' tolerance
+    const float L = (u == 1.f) ? x : log2_fast(u) * kLn2 * (x * __builtin_amdgcn_rcpf(u - 1.f));
     const float spn = fmaxf(-g, 0.f) + L, spp = fmaxf(g, 0.f) + L;  // softplus(-g), softplus(g)
     const float sp_ = (g >= 0.f) ? ru : x * ru;                     // sigmoid(g)
     const float sn_ = (g >= 0.f) ? x * ru : ru;                     // sigmoid(-g)

@@ -247,7 +247,7 @@ void bwd_combine_kernel(P p) {
 // ---------------------------------------------------------- gradient kernel
 // LDS (bytes).  Token rows [32][136] bf16 (channels permuted): Qt, Kh, Kb, dO,
 // V; transposed rows [128][40] bf16 (tokens permuted): Qt^T, Kh^T, dO^T; fp32
-// Gam of this half and of the bridged half, the decay term, the sigma of the
+// Gam (log2) of this half and 2^Gam of the bridged half, the decay term, the sigma of the
 // G^T fix-up.  The bridge operands alias Qt^T / Kh^T (written after the
 // bridge); the fp32 staging of the epilogue aliases all operand rows.
 constexpr int kRowB = kSub * kQR * 2;           // 8704
@@ -403,7 +403,7 @@ void bwd_grad_kernel(P p) {
         store_vt<2, kT32>(smem + kOffB2, cg, r, By);
         if (r == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sGamB[8 * cg + e] = lend[e];
+            for (int e = 0; e < 8; ++e) sGamB[8 * cg + e] = exp2_fast(lend[e]);
         }
     }
     if (fixG && tid < kD) sSig[tid] = p.sigG[ck * kD + tid];
@@ -446,7 +446,7 @@ void bwd_grad_kernel(P p) {
     }
     if (half) {
         // S through the first half: diag(2^{Gam0}) S_c + Kb0^T V0 (transposed accumulators)
-        const float eg = exp2_fast(sGamB[rr]);
+        const float eg = sGamB[rr];
         f32x16_t A[4];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -470,7 +470,7 @@ void bwd_grad_kernel(P p) {
         // orientations, one after the other
         {
             f32x16_t A[4];
-            const float eg = exp2_fast(sGamB[rr]);
+            const float eg = sGamB[rr];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 float x[8];
@@ -491,9 +491,11 @@ void bwd_grad_kernel(P p) {
             for (int s = 0; s < 8; ++s) {
                 float x[8];
                 unpack8(rGT[s], x);
+                const float4 g0 = *reinterpret_cast<const float4 *>(sGamB + 16 * s + 4 * h);
+                const float4 g1 = *reinterpret_cast<const float4 *>(sGamB + 16 * s + 8 + 4 * h);
+                const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    B[s >> 1][8 * (s & 1) + e] = x[e] * exp2_fast(sGamB[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)]);
+                for (int e = 0; e < 8; ++e) B[s >> 1][8 * (s & 1) + e] = x[e] * gm[e];
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
