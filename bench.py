@@ -536,6 +536,7 @@ def main():
                 "sequences": vl["sequences"], "min_len": vl["min_len"], "max_len": vl["max_len"],
                 "roofline": {"bound": "hbm", "achieved": round(vl["gbs"], 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(vl["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("prefill_varlen_N64_16K", "prefill"),
                              "algorithmic_bytes": vl["bytes"]}},
         },
     }
