@@ -247,18 +247,18 @@ void bwd_combine_kernel(P p) {
 // ---------------------------------------------------------- gradient kernel
 // LDS (bytes).  Token rows [32][136] bf16 (channels permuted): Qt, Kh, Kb, dO,
 // V; transposed rows [128][40] bf16 (tokens permuted): Qt^T, Kh^T, dO^T; fp32
-// Gam (log2) of this half and 2^Gam of the bridged half, the decay term, the sigma of the
-// G^T fix-up.  The bridge operands alias Qt^T / Kh^T (written after the
-// bridge); the fp32 staging of the epilogue aliases all operand rows.
+// 2^Gam of the bridged half, the decay term, the sigma of the G^T fix-up.  The
+// bridge operands alias Qt^T / Kh^T (written after the bridge); the fp32
+// staging of the epilogue aliases all operand rows.
 constexpr int kRowB = kSub * kQR * 2;           // 8704
 constexpr int kTB = kD * kT32 * 2;              // 10240
 constexpr int kOffQr = 0, kOffKr = kRowB, kOffKbr = 2 * kRowB, kOffDOr = 3 * kRowB, kOffVr = 4 * kRowB;
 constexpr int kOffQT = 5 * kRowB, kOffKT = kOffQT + kTB, kOffDOT = kOffKT + kTB;
-constexpr int kOffGam = kOffDOT + kTB, kOffGamB = kOffGam + kD * 4, kOffDec = kOffGamB + kD * 4;
+constexpr int kOffGamB = kOffDOT + kTB, kOffDec = kOffGamB + kD * 4;
 constexpr int kOffSig = kOffDec + kD * 4;
 constexpr int kGradLDS = kOffSig + kD * 4;
 constexpr int kOffB1 = kOffQT, kOffB2 = kOffKT;
-static_assert(4 * kSub * kSR * 4 <= kOffGam, "staging fits in the dead operand rows");
+static_assert(4 * kSub * kSR * 4 <= kOffGamB, "staging fits in the dead operand rows");
 static_assert(kGradLDS <= 80 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ bf16x8_t pack_frag(const float (&x)[8]) {
@@ -279,12 +279,11 @@ __device__ __forceinline__ uint4 fix_raw(const uint4 &x, const uint4 &y, float s
     return __builtin_bit_cast(uint4, pack_frag(a));
 }
 
-// Bridge of the first half to its checkpoint would be the identity; each
-// workgroup's own half is (c, half), the bridged one the other half of c.
+// One 32-token half (c, half) of checkpoint interval c; the other half of c is
+// the one bridged through.
 __global__ __launch_bounds__(256, 2)
 void bwd_grad_kernel(P p) {
     __shared__ __attribute__((aligned(16))) char smem[kGradLDS];
-    float *sGam = reinterpret_cast<float *>(smem + kOffGam);
     float *sGamB = reinterpret_cast<float *>(smem + kOffGamB);
     float *sDec = reinterpret_cast<float *>(smem + kOffDec);
     float *sSig = reinterpret_cast<float *>(smem + kOffSig);
@@ -368,10 +367,6 @@ void bwd_grad_kernel(P p) {
         for (int e = 0; e < 8; ++e) {
             qTp[e] = pack2(qT[e][0], qT[e][1]);
             kTp[e] = pack2(kT[e][0], kT[e][1]);
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sGam[8 * cg + e] = lend[e];
         }
     }
     // this interval's checkpoints, raw: all loads in flight at once, their
