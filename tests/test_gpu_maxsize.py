@@ -8,6 +8,11 @@ reads back the exact bf16 values of the slices it checks.
   so a ~ 4e-18 and beta ~ 1) makes the last 100 outputs and S_T depend only on
   those 100 tokens, so the oracle checks them exactly from S0 = 0.  The first
   100 outputs are checked from the start of the sequence.
+* Backward, T = 2^23 - 1 (131072 checkpoint intervals, 256 segments): reset
+  tokens at position 100 and 100 positions before the end.  The gradients of
+  the first 100 tokens and dS0 then depend only on the first 100 tokens and
+  their dO; those of the last 100 tokens only on the last 100.  The oracle's
+  backward checks both slices exactly.
 * SW-SKA, T = 2^23 - 1 at d = 128 (the largest T the entry point supports):
   rows sampled across the whole sequence, each computed by the oracle from its
   own window.
@@ -57,6 +62,35 @@ def test_prefill_max_T_reset_tail():
     # every output finite, checked on the device in slices
     for c0 in range(0, T, 1 << 21):
         assert torch.isfinite(o[:, :, c0:c0 + (1 << 21)].float()).all()
+
+
+def test_backward_max_T_reset_head_and_tail():
+    T, n = T_MAX, 100
+    log(f"backward max T={T}: inputs on the device")
+    d = _scan_inputs_on_device(T, 91)
+    dO = workloads.device_normal((1, 1, T, 128), 96)
+    tr = T - n
+    for p in (n, tr):
+        d["g"][0, 0, p].fill_(-40.0)
+        d["theta"][0, 0, p].fill_(40.0)
+    log("backward max T: GPU")
+    out = rd.rodimus_scan_backward(*(d[x] for x in NAMES), dO)
+    torch.cuda.synchronize()
+    log("backward max T: every gradient finite (on the device, in slices)")
+    for kk in ("dq", "dk", "dv", "dg", "dtau"):
+        for c0 in range(0, T, 1 << 21):
+            assert torch.isfinite(out[kk][:, :, c0:c0 + (1 << 21)]).all(), kk
+    assert torch.isfinite(out["dS0"]).all()
+    log("backward max T: oracle on the head and the tail")
+    for name, sl in (("head", slice(0, n)), ("tail", slice(tr, T))):
+        ref = oracle.scan_backward(*(host(d[x][:, :, sl]) for x in NAMES), host(dO[:, :, sl]))
+        ref["dtau"] = ref.pop("dtheta")
+        errs = {kk: err(host(out[kk][:, :, sl]), ref[kk]) for kk in ("dq", "dk", "dv", "dg", "dtau")}
+        if name == "head":
+            errs["dS0"] = err(host(out["dS0"]), ref["dS0"])
+        log(f"  {name}: " + " ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+        for kk, e in errs.items():
+            assert e <= TOL["bf16"], (name, kk, e)
 
 
 def test_swska_max_T_sampled_rows():
