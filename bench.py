@@ -1,7 +1,7 @@
 """Benchmark of the Rodimus* token-mixer hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
-                    [--only all|prefill|decode|long|swska|swska_decode|backward|varlen|copy]
+                    [--only all|prefill|decode|long|swska|swska_decode|backward|varlen|backward_varlen|copy]
 
 A step is one rodimus_scan_prefill call over the 1.6B-shaped prefill batch
 (B=4, T=4096, H=16, dk=dv=128, bf16 inputs, fp32 state, C=64) with every input
@@ -11,8 +11,8 @@ steps cycling over 8 resident input sets) is timed in the same run and
 reported as HBM GB/s and fraction of peak, as the metric asks.  The
 long-context prefill (T=131072), SW-SKA (T=32768, w=4096), the SW-SKA decode
 step, the backward of the prefill scan (same 1.6B batch) and a packed
-dynamic batch of 64 ragged requests (16384 tokens per head) are timed as
-extras.
+dynamic batch of 64 ragged requests (16384 tokens per head), forward and
+backward, are timed as extras.
 
 Timing: W untimed warm-up steps, then K steps between two HIP events on the
 stream the kernels run on (torch's current stream), with device syncs on both
@@ -195,6 +195,36 @@ def bench_varlen(cfg, steps, warmup):
     nbytes = H * total * (4 * dk * 2 + dv * 2 + dv * 2) + N * H * dk * dv * 4
     return dict(ms=ms, tokens_per_s=total / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
                 sequences=N, max_len=maxlen, min_len=int(L.min()))
+
+
+def bench_backward_varlen(cfg, steps, warmup):
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    N, H, total, dk, dv = cfg["N"], cfg["H"], cfg["total"], cfg["dk"], cfg["dv"]
+    L = workloads.ragged_lengths(cfg["seed"], N, total, cfg["min_len"])
+    x = workloads.packed_scan_inputs(cfg["seed"], H, total, dk, dv, cfg["dtype"])
+    d = {n: _dev(x[n]) for n in NAMES}
+    del x
+    dO = workloads.device_normal((H, total, dv), cfg["seed"] + 1000)
+    cu = torch.from_numpy(workloads.cu_seqlens(L)).cuda()
+    maxlen = int(L.max())
+    ws = torch.empty(rd.rodimus_scan_backward_varlen_workspace_bytes(N, H, maxlen, dk, dv, rd.BF16),
+                     dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = dict(dq=torch.empty(H, total, dk, **f32), dk=torch.empty(H, total, dk, **f32),
+               dv=torch.empty(H, total, dv, **f32), dg=torch.empty(H, total, dk, **f32),
+               dtau=torch.empty(H, total, dk, **f32), dS0=torch.empty(N, H, dk, dv, **f32))
+
+    def step():
+        rd.rodimus_scan_backward_varlen(d["q"], d["k"], d["v"], d["g"], d["theta"], dO, cu, maxlen, out=out,
+                                        workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    # per token-head the same bytes as the batched backward, plus every fp32 dS0
+    nbytes = backward_bytes(1, H, total, dk, dv) - H * dk * dv * 4 + N * H * dk * dv * 4
+    return dict(ms=ms, tokens_per_s=total / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                sequences=N, max_len=maxlen, min_len=int(L.min()), workspace_bytes=ws.numel())
 
 
 def backward_bytes(B, H, T, dk, dv):
@@ -416,7 +446,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "backward", "varlen",
-                             "copy"])
+                             "backward_varlen", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -444,6 +474,8 @@ def main():
             r = bench_backward(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup)
         elif args.only == "varlen":
             r = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
+        elif args.only == "backward_varlen":
+            r = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
         else:
             r = bench_copy()
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
@@ -467,6 +499,8 @@ def main():
     bw = bench_backward(cfg, max(5, args.steps // 2), 2)
     print("bench: prefill_varlen_N64_16K", file=sys.stderr, flush=True)
     vl = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
+    print("bench: backward_varlen_N64_16K", file=sys.stderr, flush=True)
+    bvl = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], max(5, args.steps // 2), 2)
 
     cpu = None
     if not args.no_cpu:
@@ -538,6 +572,13 @@ def main():
                              "unit": "GB/s", "frac": round(vl["gbs"] / HBM_PEAK_GBS, 4),
                              "traffic": measured_traffic("prefill_varlen_N64_16K", "prefill"),
                              "algorithmic_bytes": vl["bytes"]}},
+            "backward_varlen_N64_16K": {
+                "ms": round(bvl["ms"], 4), "tokens_per_s": round(bvl["tokens_per_s"]),
+                "sequences": bvl["sequences"], "min_len": bvl["min_len"], "max_len": bvl["max_len"],
+                "roofline": {"bound": "hbm", "achieved": round(bvl["gbs"], 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(bvl["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("backward_varlen_N64_16K", "backward"),
+                             "algorithmic_bytes": bvl["bytes"], "workspace_bytes": bvl["workspace_bytes"]}},
         },
     }
     print(json.dumps(line), flush=True)

@@ -38,7 +38,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 F32, BF16 = 0, 1
 EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill",
             "rodimus_scan_prefill_varlen_workspace_bytes", "rodimus_scan_prefill_varlen",
-            "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward", "rodimus_decode_step",
+            "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward",
+            "rodimus_scan_backward_varlen_workspace_bytes", "rodimus_scan_backward_varlen", "rodimus_decode_step",
             "sw_ska_attn", "sw_ska_decode_workspace_bytes", "sw_ska_decode_step",
             "rodimus_status_string")
 
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.rodimus_scan_backward_workspace_bytes.restype = sz
         L.rodimus_scan_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, sz, vp]
         L.rodimus_scan_backward.restype = i
+        L.rodimus_scan_backward_varlen_workspace_bytes.argtypes = [i] * 6
+        L.rodimus_scan_backward_varlen_workspace_bytes.restype = sz
+        L.rodimus_scan_backward_varlen.argtypes = [vp] * 15 + [i] * 7 + [vp, sz, vp]
+        L.rodimus_scan_backward_varlen.restype = i
         L.rodimus_decode_step.argtypes = [vp] * 8 + [i] * 5 + [vp]
         L.rodimus_decode_step.restype = i
         L.sw_ska_attn.argtypes = [vp] * 4 + [i] * 6 + [ctypes.c_float, i, vp]
@@ -247,6 +252,65 @@ def rodimus_scan_backward(q, k, v, g, tau, dO, S0=None, dS_T=None, *, want_dS0: 
                                      _ptr(out["dg"]), _ptr(out["dtau"]), _ptr(out["dS0"]), B, H, T, dk,
                                      dv, dt, _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "rodimus_scan_backward")
+    return out
+
+
+def rodimus_scan_backward_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype=BF16) -> int:
+    return int(lib().rodimus_scan_backward_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dtype))
+
+
+def rodimus_scan_backward_varlen(q, k, v, g, tau, dO, cu_seqlens, max_seqlen: int, S0=None, dS_T=None, *,
+                                 want_dS0: bool = True, out: Optional[dict] = None, workspace=None,
+                                 stream=None) -> dict:
+    """Backward of rodimus_scan_prefill_varlen over the same packed batch.
+    q, k, g, tau: [H,total,dk]; v, dO: [H,total,dv]; cu_seqlens: int32 [N+1]
+    on the device; S0, dS_T: [N,H,dk,dv] float32 or None.  Returns dict(dq,
+    dk, dv, dg, dtau) shaped like the inputs and dS0 [N,H,dk,dv], all float32;
+    `out` may supply those tensors (rows no sequence covers stay untouched)."""
+    H, total, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs N + 1 >= 1 entries")
+    for x in (k, g, tau, v, dO):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau, dO must share one dtype")
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (H, total, dk), nm)
+    _shape(v, (H, total, dv), "v")
+    _shape(dO, (H, total, dv), "dO")
+    _shape(S0, (N, H, dk, dv), "S0")
+    _shape(dS_T, (N, H, dk, dv), "dS_T")
+    for x, nm in ((S0, "S0"), (dS_T, "dS_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    f32 = dict(dtype=torch.float32, device=q.device)
+    shapes = dict(dq=(H, total, dk), dk=(H, total, dk), dv=(H, total, dv), dg=(H, total, dk),
+                  dtau=(H, total, dk), dS0=(N, H, dk, dv))
+    out = dict(out or {})
+    for nm, shp in shapes.items():
+        if out.get(nm) is None:
+            if nm != "dS0" or want_dS0:
+                out[nm] = torch.empty(shp, **f32)
+            else:
+                out[nm] = None
+        else:
+            _shape(out[nm], shp, nm)
+            if out[nm].dtype != torch.float32:
+                raise TypeError(f"{nm} must be float32")
+    need = rodimus_scan_backward_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rodimus_scan_backward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S0), _ptr(dO),
+                                            _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                            _ptr(out["dg"]), _ptr(out["dtau"]), _ptr(out["dS0"]),
+                                            _ptr(cu_seqlens), N, H, total, max_seqlen, dk, dv, dt,
+                                            _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "rodimus_scan_backward_varlen")
     return out
 
 

@@ -172,6 +172,45 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
     return hip_status();
 }
 
+size_t rodimus_scan_backward_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv, int dtype) {
+    return rodimus_scan_backward_workspace_bytes(N, H, max_seqlen, dk, dv, dtype);
+}
+
+int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, const void *g,
+                                 const void *tau, const float *S0, const void *dO, const float *dS_T,
+                                 float *dq, float *dk_, float *dv_, float *dg, float *dtau, float *dS0,
+                                 const int *cu_seqlens, int N, int H, int total_T, int max_seqlen,
+                                 int dk, int dv, int dtype, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    if (!scan_sizes_ok(N, H, max_seqlen, dk, dv, 0, dtype) || total_T < 0) return RODIMUS_ERR_INVALID_ARG;
+    if ((long long)H * total_T * (dk > dv ? dk : dv) > (1LL << 46)) return RODIMUS_ERR_INVALID_ARG;
+    if (!ok_opt_ptr(S0) || !ok_opt_ptr(dS_T) || !ok_opt_ptr(dS0) || !ok_opt_ptr(workspace))
+        return RODIMUS_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0 || H == 0) return RODIMUS_OK;
+    if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3) != 0) return RODIMUS_ERR_INVALID_ARG;
+    if (max_seqlen == 0 || total_T == 0) {  // every sequence is empty
+        if (dS0) {
+            launch_state_copy(dS_T, dS0, (size_t)N * H * dk * dv, st);
+            return hip_status();
+        }
+        return RODIMUS_OK;
+    }
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(dO) ||
+        !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
+        return RODIMUS_ERR_INVALID_ARG;
+    const bool mfma = scan_bwd_mfma_supported(max_seqlen, dk, dv, dtype);
+    const size_t need = mfma ? scan_bwd_mfma_workspace(N, H, max_seqlen) : scan_bwd_workspace(N, H, max_seqlen, dk, dv);
+    if (workspace == nullptr || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
+    ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, N, H, max_seqlen, dk, dv, dtype,
+                  workspace};
+    a.cu = cu_seqlens;
+    a.total = total_T;
+    if (mfma) launch_scan_bwd_mfma(a, st);
+    else launch_scan_bwd(a, st);
+    return hip_status();
+}
+
 int rodimus_decode_step(const void *q, const void *k, const void *v, const void *g,
                         const void *tau, const float *S_in, float *S_out, void *o,
                         int N, int H, int dk, int dv, int dtype, void *stream) {

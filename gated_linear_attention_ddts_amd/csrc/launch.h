@@ -28,6 +28,9 @@ struct ScanBwdArgs {
     float *dS0;        // nullable
     int B, H, T, dk, dv, dtype;
     void *workspace;
+    // packed variable-length batch (nullable), as in ScanArgs
+    const int *cu = nullptr;
+    int total = 0;
 };
 
 struct DecodeArgs {

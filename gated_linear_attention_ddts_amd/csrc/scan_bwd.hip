@@ -10,7 +10,8 @@
 //       final value is dS0;
 //   bwd_chunk_grads: every chunk independently, from its checkpoint pair.
 // Both state passes: one workgroup per (b,h, 64 state columns); wave w owns
-// state rows 32w .. 32w+31, lane = column.
+// state rows 32w .. 32w+31, lane = column.  In the packed layout (cu non-null)
+// every sequence runs over its own rows and chunks only (seq_rows).
 #include "launch.h"
 #include "scan_bwd_body.h"
 
@@ -25,20 +26,24 @@ template <typename Tin>
 __global__ __launch_bounds__(256)
 void bwd_states_fwd(const Tin *__restrict__ k, const Tin *__restrict__ v, const Tin *__restrict__ g,
                     const Tin *__restrict__ th, const float *__restrict__ S0, float *__restrict__ Sck,
-                    int T, int dk, int dv, int nck) {
+                    int T, int dk, int dv, int nck, const int *cu, int H, int total) {
     __shared__ float lam[kBC * kBD], mu[kBC * kBD], kb[kBC * kBD], vs[kBC * kCols];
     const int bh = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.y * kCols + l;          // state column
     const bool col = j < dv;
-    const size_t xbase = (size_t)bh * T * dk, vbase = (size_t)bh * T * dv;
+    size_t row0;
+    int len;
+    seq_rows(cu, H, total, T, bh, row0, len);
+    const size_t xbase = row0 * dk, vbase = row0 * dv;
+    const int ncl = (len + kBC - 1) / kBC;         // this sequence's chunks
     float S[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int r = 32 * w + i;
         S[i] = (S0 && col && r < dk) ? S0[((size_t)bh * dk + r) * dv + j] : 0.f;
     }
-    for (int c = 0; c < nck; ++c) {
-        const int t0 = c * kBC, L = min(kBC, T - t0);
+    for (int c = 0; c < ncl; ++c) {
+        const int t0 = c * kBC, L = min(kBC, len - t0);
         float *ck = Sck + ((size_t)bh * nck + c) * dk * dv;
         if (col) {
 #pragma unroll
@@ -75,20 +80,24 @@ template <typename Tin>
 __global__ __launch_bounds__(256)
 void bwd_states_rev(const Tin *__restrict__ q, const Tin *__restrict__ g, const Tin *__restrict__ th,
                     const Tin *__restrict__ dO, const float *__restrict__ dST, float *__restrict__ Gck,
-                    float *__restrict__ dS0, int T, int dk, int dv, int nck) {
+                    float *__restrict__ dS0, int T, int dk, int dv, int nck, const int *cu, int H, int total) {
     __shared__ float lam[kBC * kBD], mu[kBC * kBD], qt[kBC * kBD], ds[kBC * kCols];
     const int bh = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = blockIdx.y * kCols + l;
     const bool col = j < dv;
-    const size_t xbase = (size_t)bh * T * dk, vbase = (size_t)bh * T * dv;
+    size_t row0;
+    int len;
+    seq_rows(cu, H, total, T, bh, row0, len);
+    const size_t xbase = row0 * dk, vbase = row0 * dv;
+    const int ncl = (len + kBC - 1) / kBC;
     float G[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int r = 32 * w + i;
         G[i] = (dST && col && r < dk) ? dST[((size_t)bh * dk + r) * dv + j] : 0.f;
     }
-    for (int c = nck - 1; c >= 0; --c) {
-        const int t0 = c * kBC, L = min(kBC, T - t0);
+    for (int c = ncl - 1; c >= 0; --c) {
+        const int t0 = c * kBC, L = min(kBC, len - t0);
         float *ck = Gck + ((size_t)bh * nck + c) * dk * dv;
         if (col) {
 #pragma unroll
@@ -129,11 +138,17 @@ void bwd_chunk_grads(const Tin *__restrict__ q, const Tin *__restrict__ k, const
                      const Tin *__restrict__ g, const Tin *__restrict__ th, const Tin *__restrict__ dO,
                      const float *__restrict__ Sck, const float *__restrict__ Gck,
                      float *__restrict__ dq, float *__restrict__ dk_, float *__restrict__ dv_,
-                     float *__restrict__ dg, float *__restrict__ dth, int T, int dk, int dv, int nck) {
+                     float *__restrict__ dg, float *__restrict__ dth, int T, int dk, int dv, int nck,
+                     const int *cu, int H, int total) {
     __shared__ float smem[kBodyFloats];
     const int bh = blockIdx.x / nck, c = blockIdx.x % nck;
+    size_t row0;
+    int len;
+    seq_rows(cu, H, total, T, bh, row0, len);
+    if (c * kBC >= len) return;
     const size_t off = ((size_t)bh * nck + c) * dk * dv;
-    chunk_grads_body<Tin>(q, k, v, g, th, dO, Sck + off, Gck + off, dq, dk_, dv_, dg, dth, T, dk, dv, bh, c, smem);
+    chunk_grads_body<Tin>(q, k, v, g, th, dO, Sck + off, Gck + off, dq, dk_, dv_, dg, dth, row0, len, dk, dv, c,
+                          smem);
 }
 
 }  // namespace
@@ -151,13 +166,14 @@ static void launch_bwd_t(const ScanBwdArgs &a, hipStream_t st) {
     float *Gck = Sck + (size_t)BH * nck * a.dk * a.dv;
     const dim3 gs((unsigned)BH, (unsigned)((a.dv + kCols - 1) / kCols));
     hipLaunchKernelGGL(bwd_states_fwd<Tin>, gs, dim3(256), 0, st, (const Tin *)a.k, (const Tin *)a.v,
-                       (const Tin *)a.g, (const Tin *)a.tau, a.S0, Sck, a.T, a.dk, a.dv, nck);
+                       (const Tin *)a.g, (const Tin *)a.tau, a.S0, Sck, a.T, a.dk, a.dv, nck, a.cu, a.H, a.total);
     hipLaunchKernelGGL(bwd_states_rev<Tin>, gs, dim3(256), 0, st, (const Tin *)a.q, (const Tin *)a.g,
-                       (const Tin *)a.tau, (const Tin *)a.dO, a.dS_T, Gck, a.dS0, a.T, a.dk, a.dv, nck);
+                       (const Tin *)a.tau, (const Tin *)a.dO, a.dS_T, Gck, a.dS0, a.T, a.dk, a.dv, nck, a.cu,
+                       a.H, a.total);
     hipLaunchKernelGGL(bwd_chunk_grads<Tin>, dim3((unsigned)((size_t)BH * nck)), dim3(256), 0, st,
                        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.g,
                        (const Tin *)a.tau, (const Tin *)a.dO, Sck, Gck, a.dq, a.dk_, a.dv_, a.dg, a.dtau,
-                       a.T, a.dk, a.dv, nck);
+                       a.T, a.dk, a.dv, nck, a.cu, a.H, a.total);
 }
 
 void launch_scan_bwd(const ScanBwdArgs &a, hipStream_t st) {

@@ -54,6 +54,26 @@ __device__ __forceinline__ void ddts_gate_grads(float g, float th, float dla, fl
     dth = -dtau * (dla * spn + dlb * spp);
 }
 
+// Rows of sequence-head bh = s * H + h.  cu == nullptr: the batched layout,
+// rows bh * T .. bh * T + T - 1.  Otherwise the packed layout: sequence s takes
+// rows cu[s] .. cu[s+1] - 1 of head h's [total] rows, the span clamped to
+// [0, total] and to T (the longest length), so that a malformed table cannot
+// address memory outside the tensors.  bh must be wave-uniform; so are the
+// results.
+__device__ __forceinline__ void seq_rows(const int *cu, int H, int total, int T, int bh, size_t &row0,
+                                         int &len) {
+    if (cu == nullptr) {
+        row0 = (size_t)bh * T;
+        len = T;
+        return;
+    }
+    const int s = bh / H, h = bh - s * H;
+    const int a = min(max(__builtin_amdgcn_readfirstlane(cu[s]), 0), total);
+    const int b = min(max(__builtin_amdgcn_readfirstlane(cu[s + 1]), a), total);
+    row0 = (size_t)h * total + a;
+    len = min(b - a, T);
+}
+
 // Cooperative: natural-log gates of chunk tokens [t0, t0 + L) of one (b,h)
 // into lam / mu ([kBC][dk]); lam becomes the inclusive cumulative sum over the
 // chunk.  Tokens past L get lam = 0, mu = -inf.  256 threads.
@@ -81,11 +101,12 @@ __device__ __forceinline__ void chunk_gates(const Tin *g, const Tin *th, size_t 
     __syncthreads();
 }
 
-// The gradients of one chunk of kBC tokens (t0 = c * kBC) of one (b,h), given
-// S, the state entering the chunk, and G, the gradient of the state leaving
-// it (both fp32 [dk][dv], row-major).  256 threads; per-element work maps
-// thread -> channel r = tid % 128 and tokens tid / 128 + 2m.  smem holds
-// kBodyFloats floats; the caller synchronises before reusing it.
+// The gradients of one chunk of kBC tokens (t0 = c * kBC) of one sequence
+// whose len tokens occupy rows row0 .. row0+len-1 of the [rows][dk] / [rows][dv]
+// tensors, given S, the state entering the chunk, and G, the gradient of the
+// state leaving it (both fp32 [dk][dv], row-major).  256 threads; per-element
+// work maps thread -> channel r = tid % 128 and tokens tid / 128 + 2m.  smem
+// holds kBodyFloats floats; the caller synchronises before reusing it.
 constexpr int kBodyFloats = 8 * kBC * kBD + 2 * kBC * kBC + 2 * kBD;
 
 template <typename Tin>
@@ -93,13 +114,13 @@ __device__ __forceinline__ void chunk_grads_body(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v, const Tin *__restrict__ g,
     const Tin *__restrict__ th, const Tin *__restrict__ dO, const float *__restrict__ S,
     const float *__restrict__ G, float *__restrict__ dq, float *__restrict__ dk_, float *__restrict__ dv_,
-    float *__restrict__ dg, float *__restrict__ dth, int T, int dk, int dv, int bh, int c, float *smem) {
+    float *__restrict__ dg, float *__restrict__ dth, size_t row0, int len, int dk, int dv, int c, float *smem) {
     float *Q = smem, *K = Q + kBC * kBD, *V = K + kBC * kBD, *DO = V + kBC * kBD;
     float *lam = DO + kBC * kBD, *mu = lam + kBC * kBD, *X1 = mu + kBC * kBD, *X2 = X1 + kBC * kBD;
     float *dP = X2 + kBC * kBD, *A = dP + kBC * kBC, *dGam = A + kBC * kBC, *dGam2 = dGam + kBD;
     const int tid = threadIdx.x;
-    const int t0 = c * kBC, L = min(kBC, T - t0);
-    const size_t xbase = (size_t)bh * T * dk, vbase = (size_t)bh * T * dv;
+    const int t0 = c * kBC, L = min(kBC, len - t0);
+    const size_t xbase = row0 * dk, vbase = row0 * dv;
 
     // P1: inputs (zero past L) and gates
     for (int e = tid; e < kBC * dk; e += 256) {

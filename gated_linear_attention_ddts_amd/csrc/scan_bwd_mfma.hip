@@ -74,6 +74,10 @@ struct P {
     int *bad;                     // [0] = count, then entries bh * (2 nck) + half index
     float *slot;                  // [kSlowWG][2][128][128] fallback scratch
     int BH, T, nck, nseg, seg_ck;
+    // packed variable-length batch (seq_rows): sequence s = bh / H in rows
+    // cu[s] .. cu[s+1]-1 of head h = bh % H's [total] rows; T = longest length
+    const int *cu;
+    int H, total;
 };
 
 // ------------------------------------------------------------ state passes
@@ -94,16 +98,21 @@ void bwd_state_kernel(P p) {
     const int id = rev ? (int)blockIdx.x - nwg : (int)blockIdx.x;
     const int bh = uni(id % p.BH), seg = uni(id / p.BH);
     if (blockIdx.x == 0 && tid == 0) p.bad[0] = 0;
-    const int c_lo = seg * p.seg_ck, c_hi = min(p.nck, c_lo + p.seg_ck);
-    const size_t rowbase = (size_t)bh * p.T;
+    size_t rowbase;
+    int len;
+    seq_rows(p.cu, p.H, p.total, p.T, bh, rowbase, len);
+    // this segment's intervals that hold tokens of the sequence (none: the
+    // segment passes the state and its gradient through unchanged)
+    const int ncl = (len + kCk - 1) / kCk;
+    const int c_hi = min(min(p.nck, (seg + 1) * p.seg_ck), ncl), c_lo = min(seg * p.seg_ck, c_hi);
     const int r = l & 15, cg = (w << 2) | (l >> 4);
     const int rr = 32 * w + l32;  // key channel of this lane's transposed columns (role 1: also n of G)
 
     Rsrc rs;  // X operand tensor (k or q) in .k, Y operand tensor (v or dO) in .v
-    rs.k = rsrc((rev ? p.q : p.k) + rowbase * kD, p.T);
-    rs.v = rsrc((rev ? p.dO : p.v) + rowbase * kD, p.T);
-    rs.g = rsrc(p.g + rowbase * kD, p.T);
-    rs.th = rsrc(p.th + rowbase * kD, p.T);
+    rs.k = rsrc((rev ? p.q : p.k) + rowbase * kD, len);
+    rs.v = rsrc((rev ? p.dO : p.v) + rowbase * kD, len);
+    rs.g = rsrc(p.g + rowbase * kD, len);
+    rs.th = rsrc(p.th + rowbase * kD, len);
     rs.q = rs.k;
 
     f32x16_t A[4], B[4];
@@ -126,7 +135,7 @@ void bwd_state_kernel(P p) {
     Raw<kStS, false> R;
     const int nst = 2 * (c_hi - c_lo);
     const int st_first = rev ? 2 * c_hi - 1 : 2 * c_lo;
-    load_raw<kStS, false>(R, rs, st_first * kStS, r, cg);
+    if (nst > 0) load_raw<kStS, false>(R, rs, st_first * kStS, r, cg);
     for (int it = 0; it < nst; ++it) {
         const int stp = rev ? st_first - it : st_first + it;
         const int t0 = stp * kStS;
@@ -148,7 +157,7 @@ void bwd_state_kernel(P p) {
 
         // operands: X^T (Kb or Qt) and Y^T (V or dO), tokens in permuted order
         float l2a[2][8], l2b[2][8], lend[8];
-        gates_scan<kStS, false>(R, t0, p.T, r, l, l2a, l2b, lend);
+        gates_scan<kStS, false>(R, t0, len, r, l, l2a, l2b, lend);
         float xT[8][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -293,20 +302,22 @@ void bwd_grad_kernel(P p) {
     const int half = (blockIdx.x >> 3) & 1;
     if (pair >= p.BH * p.nck) return;
     const int bh = uni(pair / p.nck), c = uni(pair % p.nck);
+    size_t rowbase;
+    int len;
+    seq_rows(p.cu, p.H, p.total, p.T, bh, rowbase, len);
     const int tc = c * kCk, t0 = tc + kSub * half;
-    if (t0 >= p.T) return;
+    if (t0 >= len) return;
     const int seg = c / p.seg_ck;
     const bool fixS = seg > 0, fixG = seg < p.nseg - 1;
-    const size_t rowbase = (size_t)bh * p.T;
     const size_t ck = (size_t)bh * p.nck + c, sb = (size_t)bh * p.nseg + seg;
     const int r = l & 15, cg = (w << 2) | (l >> 4);
     const int rr = 32 * w + l32;
 
-    const __amdgpu_buffer_rsrc_t rq = rsrc(p.q + rowbase * kD, p.T), rk = rsrc(p.k + rowbase * kD, p.T);
-    const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + rowbase * kD, p.T), rg = rsrc(p.g + rowbase * kD, p.T);
-    const __amdgpu_buffer_rsrc_t rth = rsrc(p.th + rowbase * kD, p.T), rdo = rsrc(p.dO + rowbase * kD, p.T);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(p.q + rowbase * kD, len), rk = rsrc(p.k + rowbase * kD, len);
+    const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + rowbase * kD, len), rg = rsrc(p.g + rowbase * kD, len);
+    const __amdgpu_buffer_rsrc_t rth = rsrc(p.th + rowbase * kD, len), rdo = rsrc(p.dO + rowbase * kD, len);
 
-    // this half's inputs, and the other half's for the bridge (tokens past T read 0)
+    // this half's inputs, and the other half's for the bridge (tokens past the end read 0)
     uint4 Rq[2], Rk[2], Rv[2], Rg[2], Rth[2], Rdo[2], Bx[2], By[2], Bg[2], Bth[2];
     const int ts = half ? tc : tc + kSub;
     load_one<2>(Rg, rg, t0, r, cg);
@@ -329,7 +340,7 @@ void bwd_grad_kernel(P p) {
     uint32_t qTp[8], kTp[8];  // Qt^T / Kh^T rows of this lane's 8 channels, 2 tokens packed
     {
         float l2a[2][8], l2b[2][8], lend[8];
-        gates_scan_gt<kSub>(Rg, Rth, t0, p.T, r, l, l2a, l2b, lend);
+        gates_scan_gt<kSub>(Rg, Rth, t0, len, r, l, l2a, l2b, lend);
         bool bad = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) bad |= lend[e] < -kSpan2;
@@ -383,7 +394,7 @@ void bwd_grad_kernel(P p) {
     // second half -> Qt1^T, dO1^T (the gradient back through it)
     {
         float l2a[2][8], l2b[2][8], lend[8];
-        gates_scan_gt<kSub>(Bg, Bth, ts, p.T, r, l, l2a, l2b, lend);
+        gates_scan_gt<kSub>(Bg, Bth, ts, len, r, l, l2a, l2b, lend);
         float xT[8][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -521,7 +532,7 @@ void bwd_grad_kernel(P p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int j = 8 * (i >> 2) + 4 * h + (i & 3);
-            if (t0 + j < p.T) p.dv[(rowbase + t0 + j) * kD + rr] = av[i];
+            if (t0 + j < len) p.dv[(rowbase + t0 + j) * kD + rr] = av[i];
         }
     }
     __syncthreads();  // bridge operands are dead: Qt^T, Kh^T take their place
@@ -596,7 +607,7 @@ void bwd_grad_kernel(P p) {
     // The in-chunk parts of dLam use the same bf16-rounded Qt, Kh as the
     // products, so that their reverse cumulative sum telescopes exactly.
     float l2a[2][8], l2b[2][8], lend[8];
-    gates_scan_gt<kSub>(Eg, Eth, t0, p.T, r, l, l2a, l2b, lend);
+    gates_scan_gt<kSub>(Eg, Eth, t0, len, r, l, l2a, l2b, lend);
     __builtin_amdgcn_sched_barrier(0);
     load_one<2>(Eq, rq, t0, r, cg);
     load_one<2>(Ek, rk, t0, r, cg);
@@ -629,7 +640,7 @@ void bwd_grad_kernel(P p) {
             dmu[tt][e] = kf[e] * dkv[e];
             ebs[e] += kbx;
         }
-        if (t0 + t < p.T) {
+        if (t0 + t < len) {
             float *oq = p.dq + (rowbase + t0 + t) * kD + 8 * cg, *ok = p.dk + (rowbase + t0 + t) * kD + 8 * cg;
             *reinterpret_cast<float4 *>(oq) = make_float4(dqv[0], dqv[1], dqv[2], dqv[3]);
             *reinterpret_cast<float4 *>(oq + 4) = make_float4(dqv[4], dqv[5], dqv[6], dqv[7]);
@@ -661,7 +672,7 @@ void bwd_grad_kernel(P p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const int t = 2 * r + tt;
-        if (t0 + t >= p.T) continue;
+        if (t0 + t >= len) continue;
         float gf[8], tf[8], dgv[8], dtv[8];
         unpack8(Eg[tt], gf);
         unpack8(Eth[tt], tf);
@@ -695,9 +706,12 @@ void bwd_fallback_kernel(P p) {
         const int bh = ent / nsub, sub = ent % nsub, c = sub >> 1, half = sub & 1;
         const int seg = c / p.seg_ck;
         const size_t ck = (size_t)bh * p.nck + c, sb = (size_t)bh * p.nseg + seg;
-        const size_t xbase = (size_t)bh * p.T * kD;
+        size_t rowbase;
+        int len;
+        seq_rows(p.cu, p.H, p.total, p.T, bh, rowbase, len);
+        const size_t xbase = rowbase * kD;
         const int ts = c * kCk + (half ? 0 : kSub);  // the other half of the interval
-        const int Ls = min(kSub, p.T - ts);
+        const int Ls = min(kSub, len - ts);
         float *lam = smem, *mu = lam + kBC * kBD, *X = mu + kBC * kBD, *Y = X + kBC * kBD;
         chunk_gates<bf16_t>(p.g, p.th, xbase, ts, Ls, kD, lam, mu);
         for (int e = tid; e < kSub * kD; e += 256) {
@@ -733,8 +747,8 @@ void bwd_fallback_kernel(P p) {
             Gs[rr * kD + n] = gg;
         }
         __syncthreads();
-        chunk_grads_body<bf16_t>(p.q, p.k, p.v, p.g, p.th, p.dO, Ss, Gs, p.dq, p.dk, p.dv, p.dg, p.dth, p.T, kD,
-                                 kD, bh, sub, smem);
+        chunk_grads_body<bf16_t>(p.q, p.k, p.v, p.g, p.th, p.dO, Ss, Gs, p.dq, p.dk, p.dv, p.dg, p.dth, rowbase,
+                                 len, kD, kD, sub, smem);
         __syncthreads();
     }
 }
@@ -805,6 +819,7 @@ void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
     p.bad = (int *)(ws + q.o_bad);
     p.slot = (float *)(ws + q.o_slot);
     p.BH = BH; p.T = a.T; p.nck = q.nck; p.nseg = q.nseg; p.seg_ck = q.seg_ck;
+    p.cu = a.cu; p.H = a.H; p.total = a.total;
     hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(2 * BH * q.nseg)), dim3(256), 0, st, p);
     if (q.nseg > 1) {
         const size_t n = (size_t)BH * kD * kD;

@@ -8,7 +8,8 @@
  *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
  *                        whole prompt, in chunkwise-parallel form (also over
  *                        a packed batch of ragged sequences, _varlen);
- *  rodimus_scan_backward its gradients with respect to every input;
+ *  rodimus_scan_backward its gradients with respect to every input (also
+ *                        over the packed batch, _varlen);
  *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
  *  sw_ska_attn           sliding-window attention with one key matrix shared
  *                        by all heads (SW-SKA), over a whole sequence;
@@ -169,6 +170,41 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
                           float *grad_tau, float *grad_S0,
                           int B, int H, int T, int dk, int dv, int dtype,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rodimus_scan_backward over the packed batch of rodimus_scan_prefill_varlen
+ * (dynamic batching of short requests, Tupoi O(1)-memory practice guide,
+ * pwwt.cn/news/4131393, section 4.2; trained chunkwise as in the CodeFuse
+ * article's Rodimus block paragraph).  Layouts as for the packed prefill:
+ *
+ *   q, k, g, tau : [H, total_T, dk]     v, dO : [H, total_T, dv]   (dtype)
+ *   grad_q, grad_k, grad_g, grad_tau : [H, total_T, dk]   grad_v : [H, total_T, dv]
+ *                  (fp32, caller-allocated)
+ *   cu_seqlens   : int32 [N + 1], device, as for rodimus_scan_prefill_varlen
+ *   S0, dS_T, grad_S0 : [N, H, dk, dv] float, each optional (NULL) as in
+ *                  rodimus_scan_backward
+ *   max_seqlen   : at least the longest sequence; it sizes the plan, the
+ *                  workspace (rodimus_scan_backward_varlen_workspace_bytes) and
+ *                  selects the path exactly as T does for rodimus_scan_backward
+ *
+ * Each sequence gets exactly the gradients that rodimus_scan_backward gives
+ * for it alone (bitwise equal to a batched call of equal-length sequences).
+ * The table is read on the device only; each span is clamped to [0, total_T]
+ * and to max_seqlen, so a malformed table yields wrong values but no access
+ * outside the tensors.  Gradient rows that no span covers are left untouched.
+ * An empty sequence gets grad_S0 = dS_T (or zeros).  Sizes: N, H, total_T,
+ * max_seqlen >= 0; cu_seqlens 4-byte aligned and non-NULL when N, H > 0;
+ * max_seqlen = 0 or total_T = 0 copies dS_T (or zeros) into grad_S0; other
+ * rules as for rodimus_scan_backward.
+ */
+size_t rodimus_scan_backward_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,
+                                                    int dtype);
+int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, const void *g,
+                                 const void *tau, const float *S0, const void *dO, const float *dS_T,
+                                 float *grad_q, float *grad_k, float *grad_v, float *grad_g,
+                                 float *grad_tau, float *grad_S0, const int *cu_seqlens, int N, int H,
+                                 int total_T, int max_seqlen, int dk, int dv, int dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One recurrent (decode) step for N independent sequences (CodeFuse article,

@@ -241,3 +241,37 @@ def test_scan_prefill_varlen_empty_and_workspace():
     for N, H, L in ((3, 16, 4096), (64, 16, 448), (1, 1, 1)):
         assert (rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16)
                 == rd.rodimus_scan_prefill_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16))
+
+
+def bwd_varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S0=None, dO=FAKE, dST=None, dq=FAKE, dk_=FAKE,
+             dv_=FAKE, dg=FAKE, dtau=FAKE, dS0=FAKE, cu=FAKE, N=3, H=2, total=100, maxlen=64, dk=128,
+             dv=128, dtype=rd.BF16, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_backward_varlen(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S0"], a["dO"],
+                                                 a["dST"], a["dq"], a["dk_"], a["dv_"], a["dg"], a["dtau"],
+                                                 a["dS0"], a["cu"], a["N"], a["H"], a["total"], a["maxlen"],
+                                                 a["dk"], a["dv"], a["dtype"], a["ws"], a["ws_bytes"],
+                                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(dO=None), dict(dq=None), dict(dtau=None), dict(cu=None), dict(cu=FAKE + 2),
+    dict(q=MISALIGNED), dict(S0=MISALIGNED), dict(dST=MISALIGNED), dict(dS0=MISALIGNED),
+    dict(ws=MISALIGNED), dict(ws=None), dict(ws_bytes=1000),
+    dict(N=-1), dict(H=-1), dict(total=-1), dict(maxlen=-1), dict(dk=8), dict(dv=144), dict(dtype=3),
+])
+def test_scan_backward_varlen_rejects(kw):
+    assert bwd_varlen(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_scan_backward_varlen_empty_and_workspace():
+    assert bwd_varlen(N=0, q=None, cu=None, ws=None) == rd.OK
+    assert bwd_varlen(H=0, dq=None, cu=None, ws=None) == rd.OK
+    assert bwd_varlen(maxlen=0, dS0=None, q=None, ws=None) == rd.OK   # every sequence empty, nothing requested
+    assert bwd_varlen(total=0, dS0=None, q=None, ws=None) == rd.OK
+    # the plan of a packed batch is that of N sequences of the longest length
+    for N, H, L, d, dt in ((3, 16, 4096, 128, rd.BF16), (64, 16, 1131, 128, rd.BF16), (1, 1, 1, 128, rd.BF16),
+                           (5, 3, 70, 32, rd.F32)):
+        assert (rd.rodimus_scan_backward_varlen_workspace_bytes(N, H, L, d, d, dt)
+                == rd.rodimus_scan_backward_workspace_bytes(N, H, L, d, d, dt))
