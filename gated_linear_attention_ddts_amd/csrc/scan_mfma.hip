@@ -240,19 +240,29 @@ void scan_full_kernel(Params p) {
                         const float vn = bf2f(p.v[(rowbase + t) * kD + n]);
                         float part = 0.f;
 #pragma unroll
-                        for (int mt = 0; mt < 4; ++mt)
+                        for (int mt = 0; mt < 4; ++mt) {
+                            // one accumulator block at a time, as a whole: the state keeps
+                            // its MFMA registers, and this rarely taken branch does not
+                            // raise the register count of the kernel
+                            f32x16_t av, bv, qv;
 #pragma unroll
                             for (int a4 = 0; a4 < 4; ++a4) {
                                 const int i0 = tt * 128 + 32 * mt + 8 * a4 + 4 * h;
-                                const float4 av = *reinterpret_cast<const float4 *>(fa + i0);
-                                const float4 bv = *reinterpret_cast<const float4 *>(fb + i0);
-                                const float4 qv = *reinterpret_cast<const float4 *>(fq + i0);
-                                float x;
-                                x = fmaf(av.x, S[mt][4 * a4 + 0], bv.x * vn); S[mt][4 * a4 + 0] = x; part = fmaf(qv.x, x, part);
-                                x = fmaf(av.y, S[mt][4 * a4 + 1], bv.y * vn); S[mt][4 * a4 + 1] = x; part = fmaf(qv.y, x, part);
-                                x = fmaf(av.z, S[mt][4 * a4 + 2], bv.z * vn); S[mt][4 * a4 + 2] = x; part = fmaf(qv.z, x, part);
-                                x = fmaf(av.w, S[mt][4 * a4 + 3], bv.w * vn); S[mt][4 * a4 + 3] = x; part = fmaf(qv.w, x, part);
+                                const float4 x = *reinterpret_cast<const float4 *>(fa + i0);
+                                const float4 y = *reinterpret_cast<const float4 *>(fb + i0);
+                                const float4 z = *reinterpret_cast<const float4 *>(fq + i0);
+                                av[4 * a4 + 0] = x.x; av[4 * a4 + 1] = x.y; av[4 * a4 + 2] = x.z; av[4 * a4 + 3] = x.w;
+                                bv[4 * a4 + 0] = y.x; bv[4 * a4 + 1] = y.y; bv[4 * a4 + 2] = y.z; bv[4 * a4 + 3] = y.w;
+                                qv[4 * a4 + 0] = z.x; qv[4 * a4 + 1] = z.y; qv[4 * a4 + 2] = z.z; qv[4 * a4 + 3] = z.w;
                             }
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const float x = fmaf(av[i], S[mt][i], bv[i] * vn);
+                                S[mt][i] = x;
+                                part = fmaf(qv[i], x, part);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                         part += __shfl_xor(part, 32);
                         if (h == 0) p.o[(rowbase + t) * kD + n] = f2bf(part);
                     }
