@@ -543,12 +543,16 @@ def main():
             "prefill_long_T131072": {
                 "ms": round(lr["ms"], 4), "tokens_per_s": round(lr["tokens_per_s"]),
                 "roofline": {"bound": "hbm", "achieved": round(lr["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(lr["gbs"] / HBM_PEAK_GBS, 4)}},
+                             "unit": "GB/s", "frac": round(lr["gbs"] / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("prefill_long_T131072", "prefill"),
+                             "algorithmic_bytes": lr["bytes"]}},
             "swska_T32768_w4096": {
                 "ms": round(sr["ms"], 4), "tokens_per_s": round(sr["tokens_per_s"]),
                 "roofline": {"bound": "mfma", "achieved": round(sr["tflops"], 1),
                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}},
+                             "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": measured_traffic("swska_T32768_w4096", "swska"),
+                             "algorithmic_bytes": sr["bytes"]}},
             "swska_decode_N64_w4096": {
                 "us_per_step": round(sd["us_per_step"], 2), "tokens_per_s": round(sd["tokens_per_s"]),
                 "us_per_step_graph": round(sd["us_per_step_graph"], 2),
