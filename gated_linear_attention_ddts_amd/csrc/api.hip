@@ -97,7 +97,8 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
 
 size_t rodimus_scan_prefill_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,
                                                    int chunk, int dtype) {
-    return rodimus_scan_prefill_workspace_bytes(N, H, max_seqlen, dk, dv, chunk, dtype);
+    if (!scan_sizes_ok(N, H, max_seqlen, dk, dv, chunk, dtype)) return 0;
+    return rodimus_scan_prefill_workspace_bytes(N, H, max_seqlen, dk, dv, chunk, dtype) + seq_order_bytes(N);
 }
 
 int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, const void *g,
@@ -124,12 +125,16 @@ int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, con
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(o))
         return RODIMUS_ERR_INVALID_ARG;
     ScanPlan plan = plan_scan(N, H, max_seqlen, dk, dv, chunk, dtype);
-    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
-        return RODIMUS_ERR_INVALID_ARG;
+    const size_t need = plan.workspace_bytes + seq_order_bytes(N);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return RODIMUS_ERR_INVALID_ARG;
     ScanArgs a{q, k, v, g, tau, S0, o, S_T, N, H, max_seqlen, dk, dv, chunk, dtype, workspace,
                workspace_bytes};
     a.cu = cu_seqlens;
     a.total = total_T;
+    if (plan.mfma && seq_order_bytes(N) > 0) {  // longest sequences first
+        a.order = reinterpret_cast<int *>(static_cast<char *>(workspace) + plan.workspace_bytes);
+        launch_seq_order(cu_seqlens, N, total_T, max_seqlen, a.order, st);
+    }
     if (plan.mfma) launch_scan_mfma(a, plan, st);
     else launch_scan_generic(a, st);
     return hip_status();
@@ -173,7 +178,8 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
 }
 
 size_t rodimus_scan_backward_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv, int dtype) {
-    return rodimus_scan_backward_workspace_bytes(N, H, max_seqlen, dk, dv, dtype);
+    if (!scan_sizes_ok(N, H, max_seqlen, dk, dv, 0, dtype)) return 0;
+    return rodimus_scan_backward_workspace_bytes(N, H, max_seqlen, dk, dv, dtype) + seq_order_bytes(N);
 }
 
 int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, const void *g,
@@ -200,12 +206,16 @@ int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, co
         !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
         return RODIMUS_ERR_INVALID_ARG;
     const bool mfma = scan_bwd_mfma_supported(max_seqlen, dk, dv, dtype);
-    const size_t need = mfma ? scan_bwd_mfma_workspace(N, H, max_seqlen) : scan_bwd_workspace(N, H, max_seqlen, dk, dv);
-    if (workspace == nullptr || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
+    const size_t base = mfma ? scan_bwd_mfma_workspace(N, H, max_seqlen) : scan_bwd_workspace(N, H, max_seqlen, dk, dv);
+    if (workspace == nullptr || workspace_bytes < base + seq_order_bytes(N)) return RODIMUS_ERR_INVALID_ARG;
     ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, N, H, max_seqlen, dk, dv, dtype,
                   workspace};
     a.cu = cu_seqlens;
     a.total = total_T;
+    if (mfma && seq_order_bytes(N) > 0) {  // longest sequences first
+        a.order = reinterpret_cast<int *>(static_cast<char *>(workspace) + base);
+        launch_seq_order(cu_seqlens, N, total_T, max_seqlen, a.order, st);
+    }
     if (mfma) launch_scan_bwd_mfma(a, st);
     else launch_scan_bwd(a, st);
     return hip_status();

@@ -84,4 +84,13 @@ __device__ __forceinline__ void ddts_log2_gates_fast(float g, float theta, float
 
 __device__ __forceinline__ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+// Sequence-head handled by the workgroup in dispatch slot bh = pos * H + h of
+// a packed batch: the sequence at position pos of the longest-first order
+// (order null: table order).  bh must be wave-uniform; so is the result.
+__device__ __forceinline__ int seq_head(const int *order, int H, int bh) {
+    if (order == nullptr) return bh;
+    const int pos = bh / H;
+    return __builtin_amdgcn_readfirstlane(order[pos]) * H + (bh - pos * H);
+}
+
 }  // namespace rodimus

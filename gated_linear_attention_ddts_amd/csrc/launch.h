@@ -14,9 +14,11 @@ struct ScanArgs {
     void *workspace;
     size_t workspace_bytes;
     // packed variable-length batch (nullable): B sequences, sequence s in rows
-    // cu[s] .. cu[s+1]-1 of each head's [total][d] rows, T = longest length
+    // cu[s] .. cu[s+1]-1 of each head's [total][d] rows, T = longest length;
+    // order (nullable): longest-first order of the sequences
     const int *cu = nullptr;
     int total = 0;
+    int *order = nullptr;
 };
 
 struct ScanBwdArgs {
@@ -31,6 +33,7 @@ struct ScanBwdArgs {
     // packed variable-length batch (nullable), as in ScanArgs
     const int *cu = nullptr;
     int total = 0;
+    int *order = nullptr;
 };
 
 struct DecodeArgs {
@@ -59,6 +62,13 @@ struct SkaDecArgs {
     int dtype;
     void *workspace;
 };
+
+// Longest-first order of the sequences of a packed batch (seq_order.hip):
+// order[rank] = sequence, for N <= kOrderMax (else none: table order).  It sits
+// in the workspace after the plan's own bytes (seq_order_bytes(N) of them).
+constexpr int kOrderMax = 4096;
+size_t seq_order_bytes(int N);
+void launch_seq_order(const int *cu, int N, int total, int T, int *order, hipStream_t st);
 
 // Segment plan of the prefill: number of T-segments per (b,h) and workspace.
 struct ScanPlan {

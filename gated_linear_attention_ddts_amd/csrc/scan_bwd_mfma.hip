@@ -78,6 +78,7 @@ struct P {
     // cu[s] .. cu[s+1]-1 of head h = bh % H's [total] rows; T = longest length
     const int *cu;
     int H, total;
+    const int *order;  // packed batch: longest-first order of the sequences, or null
 };
 
 // ------------------------------------------------------------ state passes
@@ -93,10 +94,11 @@ void bwd_state_kernel(P p) {
     char *sX = smem, *sY = smem + kD * kT32 * 2;
     float *sGam = reinterpret_cast<float *>(smem + 2 * kD * kT32 * 2);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-    const int nwg = p.BH * p.nseg;
-    const bool rev = (int)blockIdx.x >= nwg;
-    const int id = rev ? (int)blockIdx.x - nwg : (int)blockIdx.x;
-    const int bh = uni(id % p.BH), seg = uni(id / p.BH);
+    // the two roles of one (b,h, segment) are adjacent block ids, so that in a
+    // packed batch both roles of the longest sequences are dispatched first
+    const bool rev = blockIdx.x & 1;
+    const int id = (int)(blockIdx.x >> 1);
+    const int bh = seq_head(p.order, p.H, uni(id % p.BH)), seg = uni(id / p.BH);
     if (blockIdx.x == 0 && tid == 0) p.bad[0] = 0;
     size_t rowbase;
     int len;
@@ -820,6 +822,7 @@ void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
     p.slot = (float *)(ws + q.o_slot);
     p.BH = BH; p.T = a.T; p.nck = q.nck; p.nseg = q.nseg; p.seg_ck = q.seg_ck;
     p.cu = a.cu; p.H = a.H; p.total = a.total;
+    p.order = a.cu ? a.order : nullptr;
     hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(2 * BH * q.nseg)), dim3(256), 0, st, p);
     if (q.nseg > 1) {
         const size_t n = (size_t)BH * kD * kD;

@@ -84,6 +84,7 @@ struct Params {
     // longest length (the segment plan)
     const int *cu;
     int H, total;
+    const int *order;  // packed batch: longest-first order of the sequences, or null
 };
 
 // Rows of (b,h): first row and length.  The packed form clamps each span to
@@ -114,8 +115,9 @@ void scan_full_kernel(Params p) {
     int *sCBar = sFlag + 3;                                                 // consumer-wave barrier
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-    const int bh = uni(blockIdx.x % p.BH), seg = uni(blockIdx.x / p.BH);
+    const int seg = uni(blockIdx.x / p.BH);
     if (seg >= p.G) return;
+    const int bh = VL ? seq_head(p.order, p.H, uni(blockIdx.x % p.BH)) : uni(blockIdx.x % p.BH);
     size_t rowbase;
     int Tb;
     seq_span<VL>(p, bh, rowbase, Tb);
@@ -415,8 +417,9 @@ void scan_state_kernel(Params p) {
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
     const int nsub = (p.G - 1) * p.P;
-    const int bh = uni(blockIdx.x % p.BH), sub = uni(blockIdx.x / p.BH);
+    const int sub = uni(blockIdx.x / p.BH);
     if (sub >= nsub) return;
+    const int bh = VL ? seq_head(p.order, p.H, uni(blockIdx.x % p.BH)) : uni(blockIdx.x % p.BH);
     const int seg = sub / p.P, part = sub % p.P;
     const int seg_begin = seg * p.seg_len;
     const int t_begin = seg_begin + part * p.sub_len;
@@ -560,6 +563,7 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.BH = BH; p.T = a.T; p.G = q.G; p.seg_len = q.per_seg * a.chunk; p.P = q.P;
     p.sub_len = q.sub * a.chunk;
     p.cu = a.cu; p.H = a.H; p.total = a.total;
+    p.order = a.cu ? a.order : nullptr;
     const bool vl = a.cu != nullptr;
     if (q.G > 1) {
         if (vl) hipLaunchKernelGGL(scan_state_kernel<true>, dim3(nsub * BH), dim3(256), 0, st, p);

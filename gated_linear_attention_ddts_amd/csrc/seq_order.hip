@@ -1,0 +1,63 @@
+// seq_order.hip -- longest-first order of the sequences of a packed ragged
+// batch (the dynamic batching of short requests in the Tupoi O(1)-memory
+// practice guide, section 4.2).
+//
+// The kernels that walk one sequence per workgroup (the prefill's output pass
+// and segment-state pass, the backward's state passes) run far longer for a
+// long request than for a short one.  Dispatched in table order, a long
+// request that happens to come late runs alone at the end.  This kernel ranks
+// the sequences by length, longest first (ties by index), and writes
+// order[rank] = sequence; those kernels take their sequence through it, so
+// the longest start first (list scheduling, longest job first).  All data is
+// still addressed by the sequence's own index, so results do not change.
+//
+// Lengths are those the kernels use: each span clamped to [0, total] and to T.
+// The comparison (length, then index) is a strict total order, so the ranks
+// are a permutation whatever the table holds.  Cost O(N^2) compares, spread
+// over one thread per sequence with the lengths staged through LDS; used for
+// N <= kOrderMax.
+#include "launch.h"
+
+namespace rodimus {
+
+namespace {
+
+constexpr int kTile = 1024;
+
+__device__ __forceinline__ int span_len(const int *cu, int s, int total, int T) {
+    const int a = min(max(cu[s], 0), total);
+    const int b = min(max(cu[s + 1], a), total);
+    return min(b - a, T);
+}
+
+__global__ __launch_bounds__(256)
+void seq_order_kernel(const int *__restrict__ cu, int N, int total, int T, int *__restrict__ order) {
+    __shared__ int sl[kTile];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int li = i < N ? span_len(cu, i, total, T) : 0;
+    int rank = 0;
+    for (int j0 = 0; j0 < N; j0 += kTile) {
+        const int m = min(kTile, N - j0);
+        for (int k = threadIdx.x; k < m; k += 256) sl[k] = span_len(cu, j0 + k, total, T);
+        __syncthreads();
+        if (i < N) {
+            for (int k = 0; k < m; ++k) {
+                const int lj = sl[k], j = j0 + k;
+                rank += (lj > li) | ((lj == li) & (j < i));
+            }
+        }
+        __syncthreads();
+    }
+    if (i < N) order[rank] = i;
+}
+
+}  // namespace
+
+size_t seq_order_bytes(int N) { return N > 0 && N <= kOrderMax ? ((size_t)N * 4 + 255) & ~(size_t)255 : 0; }
+
+void launch_seq_order(const int *cu, int N, int total, int T, int *order, hipStream_t st) {
+    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, cu, N, total, T,
+                       order);
+}
+
+}  // namespace rodimus

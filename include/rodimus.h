@@ -120,6 +120,10 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
  *   max_seqlen   : at least the longest sequence; it sizes the segment plan
  *                  and the workspace (query with the _workspace_bytes call)
  *
+ * The workspace also holds, for N <= 4096, the order in which the sequences
+ * are processed (longest first, computed on the device from the table), so
+ * that long requests do not start last; it never changes the results.
+ *
  * Each sequence gives exactly what rodimus_scan_prefill gives for it alone
  * (same arithmetic; bitwise equal to a batched call of equal-length
  * sequences).  The table is read on the device only: the kernels clamp each
@@ -186,6 +190,9 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
  *   max_seqlen   : at least the longest sequence; it sizes the plan, the
  *                  workspace (rodimus_scan_backward_varlen_workspace_bytes) and
  *                  selects the path exactly as T does for rodimus_scan_backward
+ *
+ * As for the packed prefill, the workspace also holds the longest-first order
+ * of the sequences (N <= 4096), which never changes the results.
  *
  * Each sequence gets exactly the gradients that rodimus_scan_backward gives
  * for it alone (bitwise equal to a batched call of equal-length sequences).

@@ -237,10 +237,21 @@ def test_scan_prefill_varlen_empty_and_workspace():
     assert varlen(H=0, o=None, cu=None) == rd.OK
     assert varlen(maxlen=0, q=None, o=None) == rd.OK      # every sequence empty, nothing to copy
     assert varlen(total=0, q=None, o=None) == rd.OK
-    # the segment plan of a packed batch is that of N sequences of the longest length
-    for N, H, L in ((3, 16, 4096), (64, 16, 448), (1, 1, 1)):
-        assert (rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16)
-                == rd.rodimus_scan_prefill_workspace_bytes(N, H, L, 128, 128, 64, rd.BF16))
+    # the segment plan of a packed batch is that of N sequences of the longest
+    # length, plus the longest-first order of the sequences (int32, 256-byte
+    # granules, up to 4096 sequences)
+    for N, H, L, d, dt in ((3, 16, 4096, 128, rd.BF16), (64, 16, 448, 128, rd.BF16), (1, 1, 1, 128, rd.BF16),
+                           (4096, 1, 8, 128, rd.BF16), (4097, 1, 8, 128, rd.BF16), (5, 3, 70, 32, rd.F32)):
+        assert (rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, L, d, d, 64, dt)
+                == rd.rodimus_scan_prefill_workspace_bytes(N, H, L, d, d, 64, dt) + _order_bytes(N))
+    assert rd.rodimus_scan_prefill_varlen_workspace_bytes(3, 2, 64, 8, 128, 64, rd.BF16) == 0   # invalid dk
+    # a workspace without room for the order is rejected
+    need = rd.rodimus_scan_prefill_varlen_workspace_bytes(3, 2, 64, 128, 128, 64, rd.BF16)
+    assert varlen(ws_bytes=need - 4) == rd.ERR_INVALID_ARG
+
+
+def _order_bytes(N):
+    return (4 * N + 255) // 256 * 256 if 0 < N <= 4096 else 0
 
 
 def bwd_varlen(**kw):
@@ -270,8 +281,11 @@ def test_scan_backward_varlen_empty_and_workspace():
     assert bwd_varlen(H=0, dq=None, cu=None, ws=None) == rd.OK
     assert bwd_varlen(maxlen=0, dS0=None, q=None, ws=None) == rd.OK   # every sequence empty, nothing requested
     assert bwd_varlen(total=0, dS0=None, q=None, ws=None) == rd.OK
-    # the plan of a packed batch is that of N sequences of the longest length
+    # the plan of a packed batch is that of N sequences of the longest length,
+    # plus the longest-first order of the sequences
     for N, H, L, d, dt in ((3, 16, 4096, 128, rd.BF16), (64, 16, 1131, 128, rd.BF16), (1, 1, 1, 128, rd.BF16),
-                           (5, 3, 70, 32, rd.F32)):
+                           (5, 3, 70, 32, rd.F32), (4097, 1, 8, 128, rd.BF16)):
         assert (rd.rodimus_scan_backward_varlen_workspace_bytes(N, H, L, d, d, dt)
-                == rd.rodimus_scan_backward_workspace_bytes(N, H, L, d, d, dt))
+                == rd.rodimus_scan_backward_workspace_bytes(N, H, L, d, d, dt) + _order_bytes(N))
+    need = rd.rodimus_scan_backward_varlen_workspace_bytes(3, 2, 64, 128, 128, rd.BF16)
+    assert bwd_varlen(ws_bytes=need - 4) == rd.ERR_INVALID_ARG

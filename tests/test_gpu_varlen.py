@@ -131,3 +131,22 @@ def test_varlen_malformed_offsets_stay_in_bounds():
     rd.rodimus_scan_prefill_varlen(dd["q"], dd["k"], dd["v"], dd["g"], dd["theta"], cu, 100, None, 64, o=o)
     torch.cuda.synchronize()
     assert torch.all(buf[H * total:] == 7.0)
+
+
+@pytest.mark.parametrize("N", [4096, 5000])
+def test_varlen_many_short_sequences(N):
+    # N = 4096: the largest batch processed longest first; N = 5000: table order
+    rng = np.random.default_rng(350 + N)
+    lengths = rng.integers(0, 10, size=N)
+    lengths[N // 2] = 200                       # one long request in the middle
+    x, cu, S0 = _packed(351, 1, lengths, 128, 128, "bf16")
+    o, ST = _run(x, cu, S0, int(lengths.max()))
+    picks = sorted({0, 1, N // 2, N - 1, *rng.integers(0, N, size=40).tolist()})
+    for s in picks:
+        a, b = int(cu[s]), int(cu[s + 1])
+        sub = [x[n].values[None, :, a:b].astype(np.float64) for n in NAMES]
+        ro, rST = oracle.scan(*sub, S0[s:s + 1].astype(np.float64))
+        es = err(ST[s:s + 1], rST)
+        eo = err(o[None, :, a:b], ro) if b > a else 0.0
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"], (N, s, b - a, eo, es)
+    log(f"  {N} sequences: {len(picks)} checked")

@@ -174,3 +174,28 @@ def test_varlen_backward_malformed_offsets_stay_in_bounds(dtype, d):
     torch.cuda.synchronize()
     for k in GRADS:
         assert torch.all(bufs[k][H * total:] == 7.0), k
+
+
+@pytest.mark.parametrize("N", [4096, 5000])
+def test_varlen_backward_many_short_sequences(N):
+    # N = 4096: the largest batch processed longest first; N = 5000: table order
+    rng = np.random.default_rng(460 + N)
+    lengths = rng.integers(0, 10, size=N)
+    lengths[N // 3] = 150
+    x, dO, cu, S0, dST = _packed(461, 1, lengths, 128, 128, "bf16")
+    out = _run(x, dO, cu, S0, dST, int(lengths.max()))
+    picks = sorted({0, N // 3, N - 1, *rng.integers(0, N, size=30).tolist()})
+    for s in picks:
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            assert np.array_equal(out["dS0"][s], dST[s].astype(np.float64)), (N, s)
+            continue
+        sub = [x[n].values[None, :, a:b].astype(np.float64) for n in NAMES]
+        ref = oracle.scan_backward(*sub, dO.values[None, :, a:b].astype(np.float64),
+                                   S0[s:s + 1].astype(np.float64), dST[s:s + 1].astype(np.float64))
+        ref["dtau"] = ref.pop("dtheta")
+        for k in GRADS:
+            e = err(out[k][None, :, a:b], ref[k])
+            assert e <= TOL["bf16"], (N, s, k, e)
+        assert err(out["dS0"][s:s + 1], ref["dS0"]) <= TOL["bf16"], (N, s)
+    log(f"  {N} sequences: {len(picks)} checked")
