@@ -14,8 +14,8 @@
 // Lengths are those the kernels use: each span clamped to [0, total] and to T.
 // The comparison (length, then index) is a strict total order, so the ranks
 // are a permutation whatever the table holds.  Cost O(N^2) compares, spread
-// over one thread per sequence with the lengths staged through LDS; used for
-// N <= kOrderMax.
+// over one thread per sequence with the lengths staged through LDS (one
+// workgroup up to 1024 sequences); used for N <= kOrderMax.
 #include "launch.h"
 
 namespace rodimus {
@@ -28,6 +28,24 @@ __device__ __forceinline__ int span_len(const int *cu, int s, int total, int T) 
     const int a = min(max(cu[s], 0), total);
     const int b = min(max(cu[s + 1], a), total);
     return min(b - a, T);
+}
+
+// N <= kTile: one workgroup; every length is loaded once, by its own thread.
+__global__ __launch_bounds__(kTile)
+void seq_order_small_kernel(const int *__restrict__ cu, int N, int total, int T, int *__restrict__ order) {
+    __shared__ int sl[kTile];
+    const int i = threadIdx.x;
+    const int li = i < N ? span_len(cu, i, total, T) : 0;
+    sl[i] = li;
+    __syncthreads();
+    if (i < N) {
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = sl[j];
+            rank += (lj > li) | ((lj == li) & (j < i));
+        }
+        order[rank] = i;
+    }
 }
 
 __global__ __launch_bounds__(256)
@@ -56,8 +74,11 @@ void seq_order_kernel(const int *__restrict__ cu, int N, int total, int T, int *
 size_t seq_order_bytes(int N) { return N > 0 && N <= kOrderMax ? ((size_t)N * 4 + 255) & ~(size_t)255 : 0; }
 
 void launch_seq_order(const int *cu, int N, int total, int T, int *order, hipStream_t st) {
-    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, cu, N, total, T,
-                       order);
+    if (N <= kTile)
+        hipLaunchKernelGGL(seq_order_small_kernel, dim3(1), dim3(kTile), 0, st, cu, N, total, T, order);
+    else
+        hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, cu, N, total, T,
+                           order);
 }
 
 }  // namespace rodimus
