@@ -71,7 +71,7 @@ void decode_step_kernel(const Tin *__restrict__ q, const Tin *__restrict__ k,
         acc.y = fmaf(qi, x.y, acc.y);
         acc.z = fmaf(qi, x.z, acc.z);
         acc.w = fmaf(qi, x.w, acc.w);
-        So[i * CG + cg] = x;
+        st_stream(&So[i * CG + cg], x);
     }
     red[rg][cg] = acc;
     __syncthreads();

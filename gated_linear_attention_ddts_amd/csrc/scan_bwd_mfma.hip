@@ -147,12 +147,12 @@ void bwd_state_kernel(P p) {
             bf16_t *dA = (rev ? p.ckG : p.ckS) + ck * kFrag;
 #pragma unroll
             for (int s = 0; s < 8; ++s)
-                *reinterpret_cast<bf16x8_t *>(dA + ((8 * w + s) * 64 + l) * 8) = cvt8(A[s >> 1], 8 * (s & 1));
+                st_stream(reinterpret_cast<bf16x8_t *>(dA + ((8 * w + s) * 64 + l) * 8), cvt8(A[s >> 1], 8 * (s & 1)));
             if (rev) {
                 bf16_t *dB = p.ckGT + ck * kFrag;
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
-                    *reinterpret_cast<bf16x8_t *>(dB + ((8 * w + s) * 64 + l) * 8) = cvt8(B[s >> 1], 8 * (s & 1));
+                    st_stream(reinterpret_cast<bf16x8_t *>(dB + ((8 * w + s) * 64 + l) * 8), cvt8(B[s >> 1], 8 * (s & 1)));
             }
             if (h == 0) (rev ? p.sigG : p.sigS)[ck * kD + rr] = exp2_fast(dacc);
         }
@@ -534,7 +534,7 @@ void bwd_grad_kernel(P p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int j = 8 * (i >> 2) + 4 * h + (i & 3);
-            if (t0 + j < len) p.dv[(rowbase + t0 + j) * kD + rr] = av[i];
+            if (t0 + j < len) st_stream(&p.dv[(rowbase + t0 + j) * kD + rr], av[i]);
         }
     }
     __syncthreads();  // bridge operands are dead: Qt^T, Kh^T take their place
@@ -644,10 +644,10 @@ void bwd_grad_kernel(P p) {
         }
         if (t0 + t < len) {
             float *oq = p.dq + (rowbase + t0 + t) * kD + 8 * cg, *ok = p.dk + (rowbase + t0 + t) * kD + 8 * cg;
-            *reinterpret_cast<float4 *>(oq) = make_float4(dqv[0], dqv[1], dqv[2], dqv[3]);
-            *reinterpret_cast<float4 *>(oq + 4) = make_float4(dqv[4], dqv[5], dqv[6], dqv[7]);
-            *reinterpret_cast<float4 *>(ok) = make_float4(dkv[0], dkv[1], dkv[2], dkv[3]);
-            *reinterpret_cast<float4 *>(ok + 4) = make_float4(dkv[4], dkv[5], dkv[6], dkv[7]);
+            st_stream(reinterpret_cast<float4 *>(oq), make_float4(dqv[0], dqv[1], dqv[2], dqv[3]));
+            st_stream(reinterpret_cast<float4 *>(oq + 4), make_float4(dqv[4], dqv[5], dqv[6], dqv[7]));
+            st_stream(reinterpret_cast<float4 *>(ok), make_float4(dkv[0], dkv[1], dkv[2], dkv[3]));
+            st_stream(reinterpret_cast<float4 *>(ok + 4), make_float4(dkv[4], dkv[5], dkv[6], dkv[7]));
         }
         __builtin_amdgcn_sched_barrier(0);  // one token at a time (register pressure)
     }
@@ -686,10 +686,10 @@ void bwd_grad_kernel(P p) {
             ddts_gate_grads(gf[e], tf[e], dl[tt][e], dmu[tt][e], dgv[e], dtv[e]);
         }
         float *og = p.dg + (rowbase + t0 + t) * kD + 8 * cg, *ot = p.dth + (rowbase + t0 + t) * kD + 8 * cg;
-        *reinterpret_cast<float4 *>(og) = make_float4(dgv[0], dgv[1], dgv[2], dgv[3]);
-        *reinterpret_cast<float4 *>(og + 4) = make_float4(dgv[4], dgv[5], dgv[6], dgv[7]);
-        *reinterpret_cast<float4 *>(ot) = make_float4(dtv[0], dtv[1], dtv[2], dtv[3]);
-        *reinterpret_cast<float4 *>(ot + 4) = make_float4(dtv[4], dtv[5], dtv[6], dtv[7]);
+        st_stream(reinterpret_cast<float4 *>(og), make_float4(dgv[0], dgv[1], dgv[2], dgv[3]));
+        st_stream(reinterpret_cast<float4 *>(og + 4), make_float4(dgv[4], dgv[5], dgv[6], dgv[7]));
+        st_stream(reinterpret_cast<float4 *>(ot), make_float4(dtv[0], dtv[1], dtv[2], dtv[3]));
+        st_stream(reinterpret_cast<float4 *>(ot + 4), make_float4(dtv[4], dtv[5], dtv[6], dtv[7]));
     }
 }
 
