@@ -259,8 +259,9 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
 static bool ska_decode_sizes_ok(int N, int H, int dk, int dv, int window, int dtype) {
     if (N < 0 || H < 0 || window < 1 || window > (1 << 19)) return false;
     if (!ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype)) return false;
-    // grids and element counts must fit the kernels' index arithmetic
-    if ((long long)N * H > (1LL << 30) || (long long)N * ((window + 127) / 128) > (1LL << 30)) return false;
+    // grids (below 2^32 work-items per launch) and element counts must fit the
+    // kernels' index arithmetic
+    if ((long long)N * H >= (1LL << 24) || swska_decode_blocks(N, H, window) >= (1u << 24)) return false;
     if ((long long)N * H * window * (dk > dv ? dk : dv) > (1LL << 46)) return false;
     return true;
 }

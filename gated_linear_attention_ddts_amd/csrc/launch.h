@@ -91,6 +91,7 @@ bool swska_supported(int T, int dk, int dv, int dtype);
 void launch_swska(const SkaArgs &a, hipStream_t st);
 bool swska_decode_supported(int dk, int dv, int dtype);
 size_t swska_decode_workspace(int N, int H, int dv, int window);
+size_t swska_decode_blocks(int N, int H, int window);   // workgroups of the split kernel
 void launch_swska_decode(const SkaDecArgs &a, hipStream_t st);
 
 }  // namespace rodimus

@@ -18,23 +18,22 @@
 //
 // The step is bound by HBM bytes: every head reads its whole value window
 // (window x dv bf16) and the key window once per sequence, for about two flops
-// per byte.  The value contraction runs on the VALU in fp32; the scores, a
-// small (key block x heads) product per sequence, on the matrix cores with
-// fp32 accumulation.  Three kernels:
+// per byte.  Both contractions run on the VALU in fp32.  Two kernels:
 //
-//   swska_decode_scores: workgroup (n, 128-slot block).  The owner of the new
-//       token's slot appends k_new / v_new to the caches.  The block's keys
-//       are loaded once into MFMA operand registers (k_new for the new slot,
-//       which no other workgroup reads) and scored against every head's query
-//       on the matrix cores (keys x heads, 32 heads per tile); scores (scaled
-//       to base 2) go to the workspace, -inf for slots outside the window.
-//       The key window is read once for all heads.
-//   swska_decode_values: workgroup (n, h, 256-slot split), few registers so
-//       that many are resident: the split's base-2 softmax weights relative
-//       to its own maximum, then the head's value rows streamed with 16-byte
-//       loads (16 lanes per row, several rows in flight per thread), reduced
-//       through LDS.  It writes per (n, h, split) the maximum m, the sum l and
-//       the unnormalised fp32 output.
+//   swska_decode_split: workgroup (n, h, 256-slot split), few registers so
+//       that many are resident.  It scores the split's keys against q[n,h]
+//       (each key row read as 16-byte column slices by consecutive lanes,
+//       whose partial dot products are summed across those lanes), forms the
+//       base-2 softmax weights relative to the split's own maximum, then
+//       streams the head's value rows with 16-byte loads (16 lanes per row,
+//       several rows in flight per thread), reduced through LDS.  It writes
+//       per (n, h, split) the maximum m, the sum l and the unnormalised fp32
+//       output.  The H workgroups of one (n, split) are consecutive on one
+//       XCD, so the split's keys come from HBM once and from that XCD's L2
+//       for the other heads.  The workgroups of the split that holds the new
+//       token's slot append v_new (and, for head 0, k_new) to the caches and
+//       read that row from k_new / v_new, so no workgroup reads a cache row
+//       that this step writes.
 //   swska_decode_combine: per (n, h, channel), merges the splits with the
 //       rescaling by 2^(m_s - max m) and normalises; one thread per sequence
 //       then advances pos[n].
@@ -45,7 +44,6 @@ namespace rodimus {
 
 namespace {
 
-constexpr int kSlots = 128;     // slots per scoring workgroup
 constexpr int kSplit = 256;     // slots per value workgroup
 constexpr int kMaxSplits = 1 << 11;  // window <= kSplit * kMaxSplits = 524288
 
@@ -84,129 +82,120 @@ __device__ __forceinline__ Geo geometry(const int *pos, int n, int W) {
     return Geo{t % W, (t + 1 >= W) ? W : t + 1};
 }
 
-// S = Q K^T on v_mfma_f32_32x32x16_bf16: A[m][k] sits in lane m + 32*(k/8),
-// element k%8; B[k][n] in lane n + 32*(k/8), element k%8; C[m][n] in lane
-// n + 32*((m/4)%2), register 4*(m/8) + m%4.  Heads on M, keys (slots) on N, so
-// that a score row is stored by consecutive lanes: each lane loads its slot's
-// key fragments straight into registers (no LDS, no barrier), and the wave
-// reuses them for every group of 32 heads.
+// Workgroups b: XCD x = b mod 8 takes the pairs (n, split) x, x + 8, ..., the
+// H heads of a pair in consecutive workgroups of that XCD.  Thread (r, c) takes
+// the split's rows r, r + RP, ... and their 16-byte column slice c: per group
+// of G rows it loads the key and value slices together, sums the key slice's
+// dot product with q over the VEC lanes of the row, and folds the rows into a
+// running maximum, sum and output (base 2).  The RP row threads are merged
+// through LDS at the end.
 template <int D>
 __global__ __launch_bounds__(256)
-void swska_decode_scores(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,
-                         const bf16_t *__restrict__ v_new, bf16_t *__restrict__ k_cache,
-                         bf16_t *__restrict__ v_cache, const int *__restrict__ pos,
-                         float *__restrict__ scores, int H, int W, int Wp, int S, float scale_log2e) {
+void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,
+                        const bf16_t *__restrict__ v_new, bf16_t *__restrict__ k_cache,
+                        bf16_t *__restrict__ v_cache, const int *__restrict__ pos,
+                        float *__restrict__ part, int N, int H, int W, int S, float scale_log2e) {
     using C = Dec<D>;
-    const int n = blockIdx.x / S, s = blockIdx.x % S, tid = threadIdx.x;
-    const Geo g = geometry(pos, n, W);
-    const int j0 = s * kSlots;
-    const int nsl = min(kSlots, W - j0);          // slots of this block
-    const size_t kc = (size_t)n * W * D;          // this sequence's key window
-    const bf16_t *kn = k_new + (size_t)n * D;
-
-    // this lane's slot (A row) and key fragments; the new slot reads k_new,
-    // slots outside the window are zero (and masked below)
-    const int w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
-    const int j = 32 * w + l32, slot = j0 + j;
-    const bool inwin = j < nsl && slot < g.nvalid;
-    const bf16_t *krow = (slot == g.jnew) ? kn : k_cache + kc + (size_t)slot * D;
-    bf16x8_t a[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        const uint4 x = inwin ? *reinterpret_cast<const uint4 *>(krow + 16 * st + 8 * hl) : make_uint4(0, 0, 0, 0);
-        a[st] = __builtin_bit_cast(bf16x8_t, x);
-    }
-
-    // the owner of the new slot appends k_new / v_new to the caches (no lane
-    // reads that cache row: the slot's fragments come from k_new)
-    if (g.jnew >= j0 && g.jnew < j0 + nsl) {
-        for (int e = tid; e < C::VEC; e += 256)
-            reinterpret_cast<uint4 *>(k_cache + kc + (size_t)g.jnew * D)[e] = reinterpret_cast<const uint4 *>(kn)[e];
-        for (int e = tid; e < H * C::VEC; e += 256) {
-            const int h = e / C::VEC, c = e % C::VEC;
-            reinterpret_cast<uint4 *>(v_cache + (((size_t)n * H + h) * W + g.jnew) * D)[c] =
-                reinterpret_cast<const uint4 *>(v_new + ((size_t)n * H + h) * D)[c];
-        }
-    }
-
-    for (int hg = 0; hg < H; hg += 32) {
-        const int head = hg + l32;
-        bf16x8_t qB[D / 16];
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const uint4 x = head < H ? *reinterpret_cast<const uint4 *>(q + ((size_t)n * H + head) * D + 16 * st + 8 * hl)
-                                     : make_uint4(0, 0, 0, 0);
-            qB[st] = __builtin_bit_cast(bf16x8_t, x);
-        }
-        f32x16_t acc = {};
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qB[st], a[st], acc, 0, 0, 0);
-        // register i: head hg + 8(i/4) + 4hl + i%4, slot j (this lane's)
-        if (j < nsl) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int hh = hg + 8 * (i >> 2) + 4 * hl + (i & 3);
-                if (hh < H) scores[((size_t)n * H + hh) * Wp + slot] = inwin ? acc[i] * scale_log2e : -INFINITY;
-            }
-        }
-    }
-}
-
-template <int D>
-__global__ __launch_bounds__(256)
-void swska_decode_values(const bf16_t *__restrict__ v_cache, const int *__restrict__ pos,
-                         const float *__restrict__ scores, float *__restrict__ part,
-                         int H, int W, int Wp, int S) {
-    using C = Dec<D>;
-    __shared__ float sP[kSplit];
-    __shared__ float sRed[4];
+    __shared__ float sM[C::RP], sL[C::RP];
     __shared__ __attribute__((aligned(16))) float sO[C::RP * D];
 
-    const int nh = blockIdx.x / S, s = blockIdx.x % S, n = nh / H, tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int i = (int)(blockIdx.x >> 3), pair = (i / H) * 8 + (int)(blockIdx.x & 7), h = i % H;
+    if (pair >= N * S) return;
+    const int n = pair / S, s = pair % S, nh = n * H + h, tid = threadIdx.x;
     const Geo g = geometry(pos, n, W);
     const int j0 = s * kSplit;
     const int jend = max(0, min(min(kSplit, W - j0), g.nvalid - j0));   // valid slots [0, jend)
-
-    // the split's weights relative to its own maximum
-    const float sc = tid < jend ? scores[(size_t)nh * Wp + j0 + tid] : -INFINITY;
-    const float wm = wave_max(sc);
-    if (l == 0) sRed[w] = wm;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
-    const float p = exp2_fast(sc - ((m == -INFINITY) ? 0.f : m));          // exp2(-inf) = 0
-    sP[tid] = p;
-    const float ws = wave_sum(p);
-    __syncthreads();                                                      // sRed (max) read by all
-    if (l == 0) sRed[w] = ws;
-    __syncthreads();
-    const float lsum = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
-
-    // value rows: thread -> row r (+ RP per pass), 16-byte column c
+    const int jn = g.jnew - j0;   // the new token's row, if this split holds it (then jn < jend)
     const int r = tid / C::VEC, c = tid % C::VEC;
-    const bf16_t *vrow = v_cache + ((size_t)nh * W + j0) * D + 8 * c;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int jj = r; jj < jend; jj += C::RP) {
-        float vf[8];
-        unpack8(*reinterpret_cast<const uint4 *>(vrow + (size_t)jj * D), vf);
-        const float pj = sP[jj];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e]);
+
+    // append the new token (one workgroup per cache row); this step reads
+    // that row from k_new / v_new instead
+    if (jn >= 0 && jn < kSplit && tid < C::VEC) {
+        reinterpret_cast<uint4 *>(v_cache + ((size_t)nh * W + g.jnew) * D)[tid] =
+            reinterpret_cast<const uint4 *>(v_new + (size_t)nh * D)[tid];
+        if (h == 0)
+            reinterpret_cast<uint4 *>(k_cache + ((size_t)n * W + g.jnew) * D)[tid] =
+                reinterpret_cast<const uint4 *>(k_new + (size_t)n * D)[tid];
     }
+
+    float qf[8];
+    unpack8(*reinterpret_cast<const uint4 *>(q + (size_t)nh * D + 8 * c), qf);
+    const bf16_t *krow = k_cache + ((size_t)n * W + j0) * D + 8 * c, *kn = k_new + (size_t)n * D + 8 * c;
+    const bf16_t *vrow = v_cache + ((size_t)nh * W + j0) * D + 8 * c, *vn = v_new + (size_t)nh * D + 8 * c;
+    constexpr int NP = kSplit / C::RP;   // rows per thread
+    constexpr int G = 8;                 // rows in flight per thread
+    float m = -INFINITY, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p0 = 0; p0 < NP; p0 += G) {
+        uint4 kv[G], vv[G];
+#pragma unroll
+        for (int pp = 0; pp < G; ++pp) {
+            const int jj = r + C::RP * (p0 + pp);
+            kv[pp] = vv[pp] = make_uint4(0, 0, 0, 0);
+            if (jj < jend) {
+                kv[pp] = *reinterpret_cast<const uint4 *>(jj == jn ? kn : krow + (size_t)jj * D);
+                vv[pp] = *reinterpret_cast<const uint4 *>(jj == jn ? vn : vrow + (size_t)jj * D);
+            }
+        }
+        float sj[G], mn = m;
+#pragma unroll
+        for (int pp = 0; pp < G; ++pp) {
+            float kf[8];
+            unpack8(kv[pp], kf);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+#pragma unroll
+            for (int x = C::VEC / 2; x >= 1; x >>= 1) d += __shfl_xor(d, x);
+            sj[pp] = r + C::RP * (p0 + pp) < jend ? d * scale_log2e : -INFINITY;
+            mn = fmaxf(mn, sj[pp]);
+        }
+        if (mn > -INFINITY) {   // else no valid row yet: nothing to fold
+            const float f = exp2_fast(m - mn);   // exp2(-inf) = 0
+            lsum *= f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= f;
+#pragma unroll
+            for (int pp = 0; pp < G; ++pp) {
+                const float pj = exp2_fast(sj[pp] - mn);
+                float vf[8];
+                unpack8(vv[pp], vf);
+                lsum += pj;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e]);
+            }
+            m = mn;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // G rows in flight, no more
+    }
+
+    // merge the RP row threads: the split's maximum, sum and output
     *reinterpret_cast<float4 *>(sO + r * D + 8 * c) = make_float4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<float4 *>(sO + r * D + 8 * c + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    __syncthreads();
-    float *rec = part + ((size_t)nh * S + s) * C::PSTRIDE;
-    if (tid < D) {
-        float acc = 0.f;
-#pragma unroll 8
-        for (int rr = 0; rr < C::RP; ++rr) acc += sO[rr * D + tid];
-        rec[tid] = acc;
+    if (c == 0) {
+        sM[r] = m;
+        sL[r] = lsum;
     }
-    if (tid == 0) {
-        rec[D] = m;
-        rec[D + 1] = lsum;
+    __syncthreads();
+    if (tid < D) {
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int rr = 0; rr < C::RP; ++rr) M = fmaxf(M, sM[rr]);
+        float acc = 0.f, L = 0.f;
+        if (M > -INFINITY) {
+#pragma unroll 8
+            for (int rr = 0; rr < C::RP; ++rr) {
+                const float f = exp2_fast(sM[rr] - M);
+                acc = fmaf(f, sO[rr * D + tid], acc);
+                L = fmaf(f, sL[rr], L);
+            }
+        }
+        float *rec = part + ((size_t)nh * S + s) * C::PSTRIDE;
+        rec[tid] = acc;
+        if (tid == 0) {
+            rec[D] = M;
+            rec[D + 1] = L;
+        }
     }
 }
 
@@ -250,37 +239,33 @@ bool swska_decode_supported(int dk, int dv, int dtype) {
     return dtype == 1 && dk == dv && (dk == 128 || dk == 64);
 }
 
-// Workspace: scores [N][H][Wp] fp32 (Wp = window rounded up to kSplit), then
-// the partial records [N][H][S][dv + 4] fp32.
+// Workspace: the partial records [N][H][S][dv + 4] fp32.
 static int value_splits(int window) { return (window + kSplit - 1) / kSplit; }
 
 size_t swska_decode_workspace(int N, int H, int dv, int window) {
-    const size_t S = value_splits(window), Wp = S * kSplit;
-    return (size_t)N * H * (Wp + S * (dv + 4)) * sizeof(float);
+    return (size_t)N * H * value_splits(window) * (dv + 4) * sizeof(float);
+}
+
+size_t swska_decode_blocks(int N, int H, int window) {
+    return ((size_t)N * value_splits(window) + 7) / 8 * 8 * H;
+}
+
+template <int D>
+static void launch_d(const SkaDecArgs &a, hipStream_t st) {
+    const int S = value_splits(a.window);
+    float *part = reinterpret_cast<float *>(a.workspace);
+    const dim3 g1((unsigned)swska_decode_blocks(a.N, a.H, a.window)), g2((unsigned)((size_t)a.N * a.H));
+    hipLaunchKernelGGL(swska_decode_split<D>, g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
+                       (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
+                       a.window, S, a.scale * kLog2e);
+    hipLaunchKernelGGL(swska_decode_combine<D>, g2, dim3(D), 0, st, part, (bf16_t *)a.o, a.pos, a.H, S);
 }
 
 void launch_swska_decode(const SkaDecArgs &a, hipStream_t st) {
-    const int SA = (a.window + kSlots - 1) / kSlots, S = value_splits(a.window), Wp = S * kSplit;
-    const float sl2e = a.scale * kLog2e;
-    float *scores = reinterpret_cast<float *>(a.workspace);
-    float *part = scores + (size_t)a.N * a.H * Wp;
-    const dim3 g1((unsigned)((size_t)a.N * SA)), g2((unsigned)((size_t)a.N * a.H * S)),
-        g3((unsigned)((size_t)a.N * a.H));
-    if (a.dk == 128) {
-        hipLaunchKernelGGL(swska_decode_scores<128>, g1, dim3(256), 0, st, (const bf16_t *)a.q,
-                           (const bf16_t *)a.k_new, (const bf16_t *)a.v_new, (bf16_t *)a.k_cache,
-                           (bf16_t *)a.v_cache, a.pos, scores, a.H, a.window, Wp, SA, sl2e);
-        hipLaunchKernelGGL(swska_decode_values<128>, g2, dim3(256), 0, st, (const bf16_t *)a.v_cache, a.pos,
-                           scores, part, a.H, a.window, Wp, S);
-        hipLaunchKernelGGL(swska_decode_combine<128>, g3, dim3(128), 0, st, part, (bf16_t *)a.o, a.pos, a.H, S);
-    } else {
-        hipLaunchKernelGGL(swska_decode_scores<64>, g1, dim3(256), 0, st, (const bf16_t *)a.q,
-                           (const bf16_t *)a.k_new, (const bf16_t *)a.v_new, (bf16_t *)a.k_cache,
-                           (bf16_t *)a.v_cache, a.pos, scores, a.H, a.window, Wp, SA, sl2e);
-        hipLaunchKernelGGL(swska_decode_values<64>, g2, dim3(256), 0, st, (const bf16_t *)a.v_cache, a.pos,
-                           scores, part, a.H, a.window, Wp, S);
-        hipLaunchKernelGGL(swska_decode_combine<64>, g3, dim3(64), 0, st, part, (bf16_t *)a.o, a.pos, a.H, S);
-    }
+    if (a.dk == 128)
+        launch_d<128>(a, st);
+    else
+        launch_d<64>(a, st);
 }
 
 }  // namespace rodimus

@@ -139,6 +139,9 @@ def skadec(**kw):
     dict(pos=None), dict(pos=FAKE + 2), dict(q=MISALIGNED), dict(kc=MISALIGNED), dict(ws=None),
     dict(ws_bytes=16), dict(N=-1), dict(H=-1), dict(window=0), dict(window=-5), dict(dk=7),
     dict(scale=0.0), dict(scale=float("nan")), dict(scale=float("inf")), dict(dtype=5),
+    # launches of 2^32 work-items or more: N*H sequence-heads, or 256-slot
+    # splits x heads, at 2^24
+    dict(N=1 << 22, H=4), dict(N=1 << 13, H=16, window=1 << 19),
 ])
 def test_swska_decode_rejects(kw):
     assert skadec(**kw) == rd.ERR_INVALID_ARG
@@ -153,10 +156,10 @@ def test_swska_decode_unsupported_and_empty():
 
 
 def test_swska_decode_workspace_query():
-    # per (sequence, head): the window's scores (rounded up to 256 slots), then per
-    # 256-slot split dv outputs + max + sum (+ 2 pad), all fp32
-    assert rd.sw_ska_decode_workspace_bytes(64, 16, 128, 128, 4096) == 64 * 16 * (4096 + 16 * 132) * 4
-    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 100) == 3 * 5 * (256 + 68) * 4
+    # per (sequence, head) and 256-slot split: dv outputs + max + sum (+ 2 pad), fp32
+    assert rd.sw_ska_decode_workspace_bytes(64, 16, 128, 128, 4096) == 64 * 16 * 16 * 132 * 4
+    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 100) == 3 * 5 * 68 * 4
+    assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 257) == 3 * 5 * 2 * 68 * 4
     assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 32, 100) == 0      # unsupported
     assert rd.sw_ska_decode_workspace_bytes(3, 5, 64, 64, 0) == 0        # invalid window
 
