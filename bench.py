@@ -286,9 +286,23 @@ def bench_decode(cfg, steps, warmup):
 
     ms = _time(step, steps, warmup)
     ms_graph = _graph_time(step, len(dsets), 8)
+
+    # ping-pong: S_in and S_out alternate between two buffers, so the step
+    # reads one 268 MB state and writes another (a 537 MB working set, twice the
+    # 256 MB Infinity Cache) instead of updating one in place
+    S2 = torch.zeros_like(S)
+
+    def step_pp():
+        s = dsets[state["s"] % len(dsets)]
+        a, b = (S, S2) if state["s"] % 2 == 0 else (S2, S)
+        state["s"] += 1
+        rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], a, b, o=o)
+
+    ms_pp = _time(step_pp, steps, warmup)
     nbytes = decode_bytes(N, H, dk, dv)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3)
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3,
+                us_per_step_pingpong=ms_pp * 1e3, gbs_pingpong=nbytes / (ms_pp * 1e-3) / 1e9)
 
 
 def _graph_time(step, n_capture, replays):
@@ -533,6 +547,8 @@ def main():
         "cpu_baseline": cpu,
         "decode": {"workload": "decode_N256", "us_per_step": round(dec["us_per_step"], 2),
                    "us_per_step_graph": round(dec["us_per_step_graph"], 2),
+                   "us_per_step_pingpong": round(dec["us_per_step_pingpong"], 2),
+                   "frac_pingpong": round(dec["gbs_pingpong"] / HBM_PEAK_GBS, 4),
                    "tokens_per_s": round(dec["tokens_per_s"]), "steps": dec["steps"],
                    "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
