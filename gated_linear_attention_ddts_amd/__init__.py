@@ -108,9 +108,18 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
         return None
     if not t.is_cuda:
         raise ValueError("tensors must be on the GPU")
+    if t.get_device() != torch.cuda.current_device():
+        raise ValueError("tensors must be on the current device (torch.cuda.set_device)")
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return t.data_ptr()
+
+
+def _out_dtype(t: Optional[torch.Tensor], dtype, name: str):
+    """A caller-supplied output must have the dtype the kernel writes (a
+    narrower one would be written past its end)."""
+    if t is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 def _shape(t: Optional[torch.Tensor], shape, name: str):
@@ -153,6 +162,7 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
     for x, nm in ((S0, "S0"), (S_T, "S_T")):
         if x is not None and x.dtype != torch.float32:
             raise TypeError(f"{nm} must be float32")
+    _out_dtype(o, q.dtype, "o")
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if S_T is None and want_state:
@@ -199,6 +209,7 @@ def rodimus_scan_prefill_varlen(q, k, v, g, tau, cu_seqlens, max_seqlen: int, S0
     for x, nm in ((S0, "S0"), (S_T, "S_T")):
         if x is not None and x.dtype != torch.float32:
             raise TypeError(f"{nm} must be float32")
+    _out_dtype(o, q.dtype, "o")
     if o is None:
         o = torch.empty((H, total, dv), dtype=q.dtype, device=q.device)
     if S_T is None and want_state:
@@ -324,14 +335,16 @@ def rodimus_decode_step(q, k, v, g, tau, S_in, S_out=None, *, o=None, stream=Non
         S_out = S_in
     for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
         _shape(x, (N, H, dk), nm)
+    _shape(v, (N, H, dv), "v")
+    for x in (k, v, g, tau):
         if x.dtype != q.dtype:
             raise TypeError("q, k, v, g, tau must share one dtype")
-    _shape(v, (N, H, dv), "v")
     _shape(S_in, (N, H, dk, dv), "S_in")
     _shape(S_out, (N, H, dk, dv), "S_out")
     _shape(o, (N, H, dv), "o")
     if S_in.dtype != torch.float32 or S_out.dtype != torch.float32:
         raise TypeError("the state must be float32")
+    _out_dtype(o, q.dtype, "o")
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     st = lib().rodimus_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S_in),
@@ -353,6 +366,7 @@ def sw_ska_attn(q, k_shared, v, window: int, scale: Optional[float] = None, *, o
     _shape(o, (B, H, T, dv), "o")
     if k_shared.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k_shared, v must share one dtype")
+    _out_dtype(o, q.dtype, "o")
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     st = lib().sw_ska_attn(_ptr(q), _ptr(k_shared), _ptr(v), _ptr(o), B, H, T, dk, dv, int(window),
@@ -387,6 +401,7 @@ def sw_ska_decode_step(q, k_new, v_new, k_cache, v_cache, pos, scale: Optional[f
             raise TypeError("q, k_new, v_new and the caches must share one dtype")
     if pos.dtype != torch.int32:
         raise TypeError("pos must be int32")
+    _out_dtype(o, q.dtype, "o")
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     need = sw_ska_decode_workspace_bytes(N, H, dk, dv, W, dt)
