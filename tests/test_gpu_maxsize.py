@@ -16,6 +16,11 @@ reads back the exact bf16 values of the slices it checks.
 * SW-SKA, T = 2^23 - 1 at d = 128 (the largest T the entry point supports):
   rows sampled across the whole sequence, each computed by the oracle from its
   own window.
+* SW-SKA decode at the largest window, 2^19 slots (2048 splits of 256): one
+  sequence with a full, wrapped window whose new token lands in the very last
+  slot, and one with 301 valid slots (2046 splits without any, which the
+  combine must weigh as zero).  The oracle computes each head's row over the
+  window gathered from the caches after the step.
 """
 import numpy as np
 import pytest
@@ -111,3 +116,31 @@ def test_swska_max_T_sampled_rows():
                           rows=[t - lo])
         e = err(host(o[:, :, t]), ro[:, :, t - lo])
         assert e <= TOL["bf16"], (t, e)
+
+
+def test_swska_decode_max_window():
+    N, H, d, W = 2, 2, 128, 1 << 19
+    ts = [3 * W - 1, 300]
+    log(f"swska decode max window W={W}: caches on the device")
+    kc = workloads.device_normal((N, W, d), 91)
+    vc = workloads.device_normal((N, H, W, d), 92)
+    q = workloads.device_normal((N, H, d), 93, 0.0, 1.0 / np.sqrt(d))
+    kn = workloads.device_normal((N, d), 94)
+    vn = workloads.device_normal((N, H, d), 95)
+    pos = torch.tensor(ts, dtype=torch.int32, device="cuda")
+    o = rd.sw_ska_decode_step(q, kn, vn, kc, vc, pos)
+    torch.cuda.synchronize()
+    assert pos.cpu().tolist() == [t + 1 for t in ts]
+    for n, t in enumerate(ts):
+        log(f"swska decode max window: oracle for sequence {n} (t = {t})")
+        ps = np.arange(max(0, t - W + 1), t + 1)
+        slots = torch.from_numpy(ps % W).cuda()
+        kw, vw = host(kc[n].index_select(0, slots)), host(vc[n].index_select(1, slots))
+        L = len(ps)
+        qs = np.zeros((1, H, L, d))
+        qs[0, :, -1] = host(q[n])
+        ref = oracle.swska(qs, kw[None], vw[None], W, rows=[h * L + L - 1 for h in range(H)], nthreads=8)
+        e = err(host(o[n]), ref[0, :, -1])
+        log(f"  err o {e:.3e}")
+        assert e <= TOL["bf16"], (n, t, e)
+        assert torch.equal(kc[n, t % W], kn[n]) and torch.equal(vc[n, :, t % W], vn[n])
