@@ -20,20 +20,19 @@
 // (window x dv bf16) and the key window once per sequence, for about two flops
 // per byte.  Both contractions run on the VALU in fp32.  Two kernels:
 //
-//   swska_decode_split: workgroup (n, h, 256-slot split), few registers so
-//       that many are resident.  It scores the split's keys against q[n,h]
-//       (each key row read as 16-byte column slices by consecutive lanes,
-//       whose partial dot products are summed across those lanes), forms the
-//       base-2 softmax weights relative to the split's own maximum, then
-//       streams the head's value rows with 16-byte loads (16 lanes per row,
-//       several rows in flight per thread), reduced through LDS.  It writes
-//       per (n, h, split) the maximum m, the sum l and the unnormalised fp32
-//       output.  The H workgroups of one (n, split) are consecutive on one
-//       XCD, so the split's keys come from HBM once and from that XCD's L2
-//       for the other heads.  The workgroups of the split that holds the new
-//       token's slot append v_new (and, for head 0, k_new) to the caches and
-//       read that row from k_new / v_new, so no workgroup reads a cache row
-//       that this step writes.
+//   swska_decode_split: workgroup (n, h, 256-slot split).  Each thread takes
+//       every 16th row of the split (D = 128) and one 16-byte column slice of
+//       it; per group of rows it loads the key and value slices together,
+//       sums the key slice's dot product with q[n,h] over the lanes that hold
+//       the row, and folds the rows into a running maximum, sum and output in
+//       base 2 (an online softmax per thread).  The row threads are merged
+//       through LDS into the split's record: its maximum m, sum l and
+//       unnormalised fp32 output.  The H workgroups of one (n, split) are
+//       consecutive on one XCD, so the split's keys come from HBM once and
+//       from that XCD's L2 for the other heads.  The workgroups of the split
+//       that holds the new token's slot append v_new (and, for head 0, k_new)
+//       to the caches and read that row from k_new / v_new, so no workgroup
+//       reads a cache row that this step writes.
 //   swska_decode_combine: per (n, h, channel), merges the splits with the
 //       rescaling by 2^(m_s - max m) and normalises; one thread per sequence
 //       then advances pos[n].
@@ -50,7 +49,7 @@ constexpr int kMaxSplits = 1 << 11;  // window <= kSplit * kMaxSplits = 524288
 template <int D>
 struct Dec {
     static constexpr int VEC = D / 8;          // 16-byte vectors per row
-    static constexpr int RP = 256 / VEC;       // rows per pass of the value workgroup
+    static constexpr int RP = 256 / VEC;       // row threads of the split workgroup
     static constexpr int PSTRIDE = D + 4;      // floats per partial record: o[D], m, l, pad
 };
 
