@@ -7,10 +7,11 @@
 // Fig. 4), inside sliding-window attention where each query sees the previous
 // w keys including itself (MiniCPM-SALA blog, sections 1.1 and 2.1).
 //
-// Kernel: one workgroup = 128 consecutive queries of one (b, h); 4 waves, 32
-// queries each.  Keys/values stream through LDS in tiles of 64 (double
+// Kernel: one workgroup = 32 NW consecutive queries of one (b, h); NW waves,
+// 32 queries each (NW = 8 at d = 128, one workgroup per CU; NW = 4 at d = 64,
+// two per CU).  Keys/values stream through LDS in tiles of 64 (double
 // buffered; the next tile is fetched into registers while the current one is
-// used).  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+// used), so each staged tile serves 32 NW queries.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T       keys on the M dimension, queries on lanes, so each lane
 //                     owns one query's scores and the softmax reductions stay
 //                     inside the lane (plus one exchange with lane^32);
@@ -31,7 +32,6 @@ namespace rodimus {
 
 namespace {
 
-constexpr int kBQ = 128;
 constexpr int kBK = 64;
 constexpr float kRescale = 8.f;  // log2 of the largest p before the output is rescaled
 
@@ -73,45 +73,45 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-template <int D>
+template <int D, int NT = 256>
 struct Tile {
     static constexpr int KROW = D + 8;        // bf16 per K row in LDS
     static constexpr int VROW = kBK + 8;      // bf16 per V^T row in LDS
     static constexpr int KBYTES = kBK * KROW * 2;
     static constexpr int VBYTES = D * VROW * 2;
     static constexpr int BYTES = KBYTES + VBYTES;
-    static constexpr int KVEC = kBK * D / 8 / 256;  // 16-byte K vectors per thread
-    static constexpr int KPT = D / 32;              // keys per thread in the V transpose
+    static constexpr int KVEC = kBK * D / 8 / NT;   // 16-byte K vectors per thread
+    static constexpr int KPT = 8 * D / NT;          // keys per thread in the V transpose
 };
 
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void fetch_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int k0,
-                                           uint4 (&rk)[Tile<D>::KVEC], uint4 (&rv)[Tile<D>::KPT]) {
+                                           uint4 (&rk)[Tile<D, NT>::KVEC], uint4 (&rv)[Tile<D, NT>::KPT]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < Tile<D>::KVEC; ++i) {
-        const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
+    for (int i = 0; i < Tile<D, NT>::KVEC; ++i) {
+        const int vi = tid + NT * i, row = vi / (D / 8), col = vi % (D / 8);
         rk[i] = bload(kr, (uint32_t)(k0 + row) * (D * 2u) + 16u * col);
     }
-    constexpr int KPT = Tile<D>::KPT;
+    constexpr int KPT = Tile<D, NT>::KPT;
     const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) rv[i] = bload(vr, (uint32_t)(k0 + KPT * kg + i) * (D * 2u) + 16u * dg);
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D>::KVEC],
-                                           const uint4 (&rv)[Tile<D>::KPT]) {
+template <int D, int NT>
+__device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D, NT>::KVEC],
+                                           const uint4 (&rv)[Tile<D, NT>::KPT]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < Tile<D>::KVEC; ++i) {
-        const int vi = tid + 256 * i, row = vi / (D / 8), col = vi % (D / 8);
-        *reinterpret_cast<uint4 *>(buf + (row * Tile<D>::KROW + 8 * col) * 2) = rk[i];
+    for (int i = 0; i < Tile<D, NT>::KVEC; ++i) {
+        const int vi = tid + NT * i, row = vi / (D / 8), col = vi % (D / 8);
+        *reinterpret_cast<uint4 *>(buf + (row * Tile<D, NT>::KROW + 8 * col) * 2) = rk[i];
     }
     // V^T: row = value channel, KPT consecutive keys per write
-    constexpr int KPT = Tile<D>::KPT;
+    constexpr int KPT = Tile<D, NT>::KPT;
     const int kg = tid % (kBK / KPT), dg = tid / (kBK / KPT);
-    char *vt = buf + Tile<D>::KBYTES;
+    char *vt = buf + Tile<D, NT>::KBYTES;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         // element e of keys 2i and 2i+1 -> one word (v_perm: the low or the high
@@ -125,18 +125,19 @@ __device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D>:
             const uint32_t wc = (e < 2) ? c.x : (e < 4) ? c.y : (e < 6) ? c.z : c.w;
             w[i] = __builtin_amdgcn_perm(wc, wa, sel);
         }
-        const int off = ((8 * dg + e) * Tile<D>::VROW + perm16(KPT * kg)) * 2;
+        const int off = ((8 * dg + e) * Tile<D, NT>::VROW + perm16(KPT * kg)) * 2;
         if (KPT == 4) *reinterpret_cast<uint2 *>(vt + off) = make_uint2(w[0], w[1 % (KPT / 2)]);
         else *reinterpret_cast<uint32_t *>(vt + off) = w[0];
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2)
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW)
 void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                   const bf16_t *__restrict__ v, bf16_t *__restrict__ o,
                   int BH, int H, int T, int window, float scale_log2e, int nqb) {
-    using TL = Tile<D>;
+    constexpr int NT = 64 * NW, kBQ = 32 * NW;
+    using TL = Tile<D, NT>;
     __shared__ __attribute__((aligned(16))) char smem[2 * TL::BYTES];
 
     // XCD-aware block -> (b*H + h, query block): XCD x = id % 8 walks the heads
@@ -184,14 +185,14 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int wlo = qw0 - window + 1, whi = qw0 + 31;
 
     uint4 rk[TL::KVEC], rv[TL::KPT];
-    fetch_tile<D>(kr, vr, kt0, rk, rv);
-    store_tile<D>(smem, rk, rv);
+    fetch_tile<D, NT>(kr, vr, kt0, rk, rv);
+    store_tile<D, NT>(smem, rk, rv);
     __syncthreads();
 
     int buf = 0;
     for (int k0 = kt0; k0 < hi; k0 += kBK, buf ^= 1) {
         const bool more = k0 + kBK < hi;
-        if (more) fetch_tile<D>(kr, vr, k0 + kBK, rk, rv);
+        if (more) fetch_tile<D, NT>(kr, vr, k0 + kBK, rk, rv);
         const char *cur = smem + buf * TL::BYTES;
 
         const bool skip = (k0 + kBK - 1 < wlo) || (k0 > whi);
@@ -266,7 +267,7 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                     O[mt] = mfma(a, P[s], O[mt]);
                 }
         }
-        if (more) store_tile<D>(smem + (buf ^ 1) * TL::BYTES, rk, rv);
+        if (more) store_tile<D, NT>(smem + (buf ^ 1) * TL::BYTES, rk, rv);
         __syncthreads();
     }
 
@@ -296,18 +297,19 @@ bool swska_supported(int T, int dk, int dv, int dtype) {
 
 void launch_swska(const SkaArgs &a, hipStream_t st) {
     const int BH = a.B * a.H;
-    const int nqb = (a.T + kBQ - 1) / kBQ;
     const float sl2e = a.scale * kLog2e;
     const int window = a.window < a.T ? a.window : a.T;  // w >= T: every earlier key
-    dim3 grid((unsigned)(BH * nqb));
-    if (a.dk == 128)
-        hipLaunchKernelGGL(swska_kernel<128>, grid, dim3(256), 0, st, (const bf16_t *)a.q,
+    if (a.dk == 128) {
+        const int nqb = (a.T + 255) / 256;
+        hipLaunchKernelGGL((swska_kernel<128, 8>), dim3((unsigned)(BH * nqb)), dim3(512), 0, st, (const bf16_t *)a.q,
                            (const bf16_t *)a.k, (const bf16_t *)a.v, (bf16_t *)a.o, BH, a.H, a.T,
                            window, sl2e, nqb);
-    else
-        hipLaunchKernelGGL(swska_kernel<64>, grid, dim3(256), 0, st, (const bf16_t *)a.q,
+    } else {
+        const int nqb = (a.T + 127) / 128;
+        hipLaunchKernelGGL((swska_kernel<64, 4>), dim3((unsigned)(BH * nqb)), dim3(256), 0, st, (const bf16_t *)a.q,
                            (const bf16_t *)a.k, (const bf16_t *)a.v, (bf16_t *)a.o, BH, a.H, a.T,
                            window, sl2e, nqb);
+    }
 }
 
 }  // namespace rodimus
