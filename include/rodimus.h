@@ -272,8 +272,10 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
  * window) are never read.  A negative pos is treated as 0.
  *
  * Supported: RODIMUS_BF16 with dk = dv = 128 or 64 (else
- * RODIMUS_ERR_UNSUPPORTED); scale finite and > 0; 1 <= window <= 524288
- * (else RODIMUS_ERR_INVALID_ARG).  All buffers
+ * RODIMUS_ERR_UNSUPPORTED); scale finite and > 0; 1 <= window <= 524288;
+ * N * H < 2^24 and N * ceil(window / 256) * H below about 2^24 (one
+ * workgroup per sequence, head and 256-slot split; a launch stays below 2^32
+ * work-items) (else RODIMUS_ERR_INVALID_ARG).  All buffers
  * are caller-owned device memory, 16-byte aligned (pos: 4-byte aligned).
  * `workspace` holds per-split partial results: at least
  * sw_ska_decode_workspace_bytes(N, H, dk, dv, window, dtype) bytes, else
