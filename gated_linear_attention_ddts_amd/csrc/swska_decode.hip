@@ -20,19 +20,21 @@
 // (window x dv bf16) and the key window once per sequence, for about two flops
 // per byte.  Both contractions run on the VALU in fp32.  Two kernels:
 //
-//   swska_decode_split: workgroup (n, h, 256-slot split).  Each thread takes
-//       every 16th row of the split (D = 128) and one 16-byte column slice of
-//       it; per group of rows it loads the key and value slices together,
-//       sums the key slice's dot product with q[n,h] over the lanes that hold
-//       the row, and folds the rows into a running maximum, sum and output in
-//       base 2 (an online softmax per thread).  The row threads are merged
-//       through LDS into the split's record: its maximum m, sum l and
-//       unnormalised fp32 output.  The H workgroups of one (n, split) are
-//       consecutive on one XCD, so the split's keys come from HBM once and
-//       from that XCD's L2 for the other heads.  The workgroups of the split
-//       that holds the new token's slot append v_new (and, for head 0, k_new)
-//       to the caches and read that row from k_new / v_new, so no workgroup
-//       reads a cache row that this step writes.
+//   swska_decode_split: workgroup (n, HP heads, 256-slot split), HP = 2 when
+//       H is even (else 1), so that each key slice loaded serves HP heads.
+//       Each thread takes every 16th row of the split (D = 128) and one
+//       16-byte column slice of it; per group of rows it loads the key slice
+//       and the HP value slices together, sums each head's dot product over
+//       the lanes that hold the row, and folds the rows into a running
+//       maximum, sum and output per head in base 2 (an online softmax per
+//       thread).  The row threads are merged through LDS into each head's
+//       record for the split: its maximum m, sum l and unnormalised fp32
+//       output.  The H / HP workgroups of one (n, split) are consecutive on
+//       one XCD, so the split's keys come from HBM once and from that XCD's
+//       L2 for the other heads.  The workgroups of the split that holds the
+//       new token's slot append v_new (and, for head 0, k_new) to the caches
+//       and read that row from k_new / v_new, so no workgroup reads a cache
+//       row that this step writes.
 //   swska_decode_combine: per (n, h, channel), merges the splits with the
 //       rescaling by 2^(m_s - max m) and normalises; one thread per sequence
 //       then advances pos[n].
@@ -88,110 +90,147 @@ __device__ __forceinline__ Geo geometry(const int *pos, int n, int W) {
 // dot product with q over the VEC lanes of the row, and folds the rows into a
 // running maximum, sum and output (base 2).  The RP row threads are merged
 // through LDS at the end.
-template <int D>
+// Workgroups b: XCD x = b mod 8 takes the pairs (n, split) x, x + 8, ..., the
+// H / HP head groups of a pair in consecutive workgroups of that XCD.
+template <int D, int HP>
 __global__ __launch_bounds__(256)
 void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,
                         const bf16_t *__restrict__ v_new, bf16_t *__restrict__ k_cache,
                         bf16_t *__restrict__ v_cache, const int *__restrict__ pos,
                         float *__restrict__ part, int N, int H, int W, int S, float scale_log2e) {
     using C = Dec<D>;
-    __shared__ float sM[C::RP], sL[C::RP];
-    __shared__ __attribute__((aligned(16))) float sO[C::RP * D];
+    __shared__ float sM[HP][C::RP], sL[HP][C::RP];
+    __shared__ __attribute__((aligned(16))) float sO[HP][C::RP * D];
 
-    const int i = (int)(blockIdx.x >> 3), pair = (i / H) * 8 + (int)(blockIdx.x & 7), h = i % H;
+    const int HG = H / HP;   // head groups (H is a multiple of HP)
+    const int i = (int)(blockIdx.x >> 3), pair = (i / HG) * 8 + (int)(blockIdx.x & 7), h0 = (i % HG) * HP;
     if (pair >= N * S) return;
-    const int n = pair / S, s = pair % S, nh = n * H + h, tid = threadIdx.x;
+    const int n = pair / S, s = pair % S, tid = threadIdx.x;
     const Geo g = geometry(pos, n, W);
     const int j0 = s * kSplit;
-    const int jend = max(0, min(min(kSplit, W - j0), g.nvalid - j0));   // valid slots [0, jend)
+    const int jend = max(0, min(min(kSplit, W - j0), g.nvalid - j0));
     const int jn = g.jnew - j0;   // the new token's row, if this split holds it (then jn < jend)
-    const int r = tid / C::VEC, c = tid % C::VEC;
+    const int r = tid / C::VEC, c = tid % C::VEC;   // rows r, r + RP, ...; 16-byte column c
 
     // append the new token (one workgroup per cache row); this step reads
     // that row from k_new / v_new instead
     if (jn >= 0 && jn < kSplit && tid < C::VEC) {
-        reinterpret_cast<uint4 *>(v_cache + ((size_t)nh * W + g.jnew) * D)[tid] =
-            reinterpret_cast<const uint4 *>(v_new + (size_t)nh * D)[tid];
-        if (h == 0)
+#pragma unroll
+        for (int hh = 0; hh < HP; ++hh) {
+            const size_t nh = (size_t)n * H + h0 + hh;
+            reinterpret_cast<uint4 *>(v_cache + (nh * W + g.jnew) * D)[tid] =
+                reinterpret_cast<const uint4 *>(v_new + nh * D)[tid];
+        }
+        if (h0 == 0)
             reinterpret_cast<uint4 *>(k_cache + ((size_t)n * W + g.jnew) * D)[tid] =
                 reinterpret_cast<const uint4 *>(k_new + (size_t)n * D)[tid];
     }
 
-    float qf[8];
-    unpack8(*reinterpret_cast<const uint4 *>(q + (size_t)nh * D + 8 * c), qf);
+    float qf[HP][8];
+    const bf16_t *vrow[HP], *vn[HP];
+#pragma unroll
+    for (int hh = 0; hh < HP; ++hh) {
+        const size_t nh = (size_t)n * H + h0 + hh;
+        unpack8(*reinterpret_cast<const uint4 *>(q + nh * D + 8 * c), qf[hh]);
+        vrow[hh] = v_cache + (nh * W + j0) * D + 8 * c;
+        vn[hh] = v_new + nh * D + 8 * c;
+    }
     const bf16_t *krow = k_cache + ((size_t)n * W + j0) * D + 8 * c, *kn = k_new + (size_t)n * D + 8 * c;
-    const bf16_t *vrow = v_cache + ((size_t)nh * W + j0) * D + 8 * c, *vn = v_new + (size_t)nh * D + 8 * c;
     constexpr int NP = kSplit / C::RP;   // rows per thread
-    constexpr int G = 8;                 // rows in flight per thread
-    float m = -INFINITY, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int G = 4;                 // rows in flight per thread
+    float m[HP], lsum[HP], o[HP][8];
+#pragma unroll
+    for (int hh = 0; hh < HP; ++hh) {
+        m[hh] = -INFINITY;
+        lsum[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    }
 #pragma unroll
     for (int p0 = 0; p0 < NP; p0 += G) {
-        uint4 kv[G], vv[G];
+        uint4 kv[G], vv[HP][G];
 #pragma unroll
         for (int pp = 0; pp < G; ++pp) {
             const int jj = r + C::RP * (p0 + pp);
-            kv[pp] = vv[pp] = make_uint4(0, 0, 0, 0);
+            kv[pp] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int hh = 0; hh < HP; ++hh) vv[hh][pp] = make_uint4(0, 0, 0, 0);
             if (jj < jend) {
                 kv[pp] = *reinterpret_cast<const uint4 *>(jj == jn ? kn : krow + (size_t)jj * D);
-                vv[pp] = *reinterpret_cast<const uint4 *>(jj == jn ? vn : vrow + (size_t)jj * D);
+#pragma unroll
+                for (int hh = 0; hh < HP; ++hh)
+                    vv[hh][pp] = *reinterpret_cast<const uint4 *>(jj == jn ? vn[hh] : vrow[hh] + (size_t)jj * D);
             }
         }
-        float sj[G], mn = m;
+        float sj[HP][G], mn[HP];
+#pragma unroll
+        for (int hh = 0; hh < HP; ++hh) mn[hh] = m[hh];
 #pragma unroll
         for (int pp = 0; pp < G; ++pp) {
             float kf[8];
             unpack8(kv[pp], kf);
-            float d = 0.f;
+            const bool ok = r + C::RP * (p0 + pp) < jend;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+            for (int hh = 0; hh < HP; ++hh) {
+                float d = 0.f;
 #pragma unroll
-            for (int x = C::VEC / 2; x >= 1; x >>= 1) d += __shfl_xor(d, x);
-            sj[pp] = r + C::RP * (p0 + pp) < jend ? d * scale_log2e : -INFINITY;
-            mn = fmaxf(mn, sj[pp]);
-        }
-        if (mn > -INFINITY) {   // else no valid row yet: nothing to fold
-            const float f = exp2_fast(m - mn);   // exp2(-inf) = 0
-            lsum *= f;
+                for (int e = 0; e < 8; ++e) d = fmaf(qf[hh][e], kf[e], d);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= f;
-#pragma unroll
-            for (int pp = 0; pp < G; ++pp) {
-                const float pj = exp2_fast(sj[pp] - mn);
-                float vf[8];
-                unpack8(vv[pp], vf);
-                lsum += pj;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf(pj, vf[e], o[e]);
+                for (int x = C::VEC / 2; x >= 1; x >>= 1) d += __shfl_xor(d, x);
+                sj[hh][pp] = ok ? d * scale_log2e : -INFINITY;
+                mn[hh] = fmaxf(mn[hh], sj[hh][pp]);
             }
-            m = mn;
+        }
+#pragma unroll
+        for (int hh = 0; hh < HP; ++hh) {
+            if (mn[hh] > -INFINITY) {   // else no valid row yet: nothing to fold
+                const float f = exp2_fast(m[hh] - mn[hh]);   // exp2(-inf) = 0
+                lsum[hh] *= f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[hh][e] *= f;
+#pragma unroll
+                for (int pp = 0; pp < G; ++pp) {
+                    const float pj = exp2_fast(sj[hh][pp] - mn[hh]);
+                    float vf[8];
+                    unpack8(vv[hh][pp], vf);
+                    lsum[hh] += pj;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pj, vf[e], o[hh][e]);
+                }
+                m[hh] = mn[hh];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);   // G rows in flight, no more
     }
 
-    // merge the RP row threads: the split's maximum, sum and output
-    *reinterpret_cast<float4 *>(sO + r * D + 8 * c) = make_float4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<float4 *>(sO + r * D + 8 * c + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    if (c == 0) {
-        sM[r] = m;
-        sL[r] = lsum;
+    // merge the RP row threads of each head: the split's maximum, sum and output
+#pragma unroll
+    for (int hh = 0; hh < HP; ++hh) {
+        *reinterpret_cast<float4 *>(&sO[hh][r * D + 8 * c]) = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
+        *reinterpret_cast<float4 *>(&sO[hh][r * D + 8 * c + 4]) = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+        if (c == 0) {
+            sM[hh][r] = m[hh];
+            sL[hh][r] = lsum[hh];
+        }
     }
     __syncthreads();
-    if (tid < D) {
+    for (int idx = tid; idx < HP * D; idx += 256) {
+        const int hh = idx / D, d = idx % D;
         float M = -INFINITY;
 #pragma unroll 8
-        for (int rr = 0; rr < C::RP; ++rr) M = fmaxf(M, sM[rr]);
+        for (int rr = 0; rr < C::RP; ++rr) M = fmaxf(M, sM[hh][rr]);
         float acc = 0.f, L = 0.f;
         if (M > -INFINITY) {
 #pragma unroll 8
             for (int rr = 0; rr < C::RP; ++rr) {
-                const float f = exp2_fast(sM[rr] - M);
-                acc = fmaf(f, sO[rr * D + tid], acc);
-                L = fmaf(f, sL[rr], L);
+                const float f = exp2_fast(sM[hh][rr] - M);
+                acc = fmaf(f, sO[hh][rr * D + d], acc);
+                L = fmaf(f, sL[hh][rr], L);
             }
         }
-        float *rec = part + ((size_t)nh * S + s) * C::PSTRIDE;
-        rec[tid] = acc;
-        if (tid == 0) {
+        float *rec = part + (((size_t)n * H + h0 + hh) * S + s) * C::PSTRIDE;
+        rec[d] = acc;
+        if (d == 0) {
             rec[D] = M;
             rec[D + 1] = L;
         }
@@ -253,10 +292,18 @@ template <int D>
 static void launch_d(const SkaDecArgs &a, hipStream_t st) {
     const int S = value_splits(a.window);
     float *part = reinterpret_cast<float *>(a.workspace);
-    const dim3 g1((unsigned)swska_decode_blocks(a.N, a.H, a.window)), g2((unsigned)((size_t)a.N * a.H));
-    hipLaunchKernelGGL(swska_decode_split<D>, g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
-                       (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
-                       a.window, S, a.scale * kLog2e);
+    const dim3 g2((unsigned)((size_t)a.N * a.H));
+    if (a.H % 2 == 0) {
+        const dim3 g1((unsigned)(swska_decode_blocks(a.N, a.H, a.window) / 2));
+        hipLaunchKernelGGL((swska_decode_split<D, 2>), g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
+                           (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
+                           a.window, S, a.scale * kLog2e);
+    } else {
+        const dim3 g1((unsigned)swska_decode_blocks(a.N, a.H, a.window));
+        hipLaunchKernelGGL((swska_decode_split<D, 1>), g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
+                           (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
+                           a.window, S, a.scale * kLog2e);
+    }
     hipLaunchKernelGGL(swska_decode_combine<D>, g2, dim3(D), 0, st, part, (bf16_t *)a.o, a.pos, a.H, S);
 }
 
