@@ -46,7 +46,6 @@ namespace rodimus {
 namespace {
 
 constexpr int kSplit = 256;     // slots per value workgroup
-constexpr int kMaxSplits = 1 << 11;  // window <= kSplit * kMaxSplits = 524288
 
 template <int D>
 struct Dec {
@@ -60,17 +59,6 @@ __device__ __forceinline__ void unpack8(const uint4 &x, float *f) {
     f[2] = __uint_as_float(x.y << 16); f[3] = __uint_as_float(x.y & 0xffff0000u);
     f[4] = __uint_as_float(x.z << 16); f[5] = __uint_as_float(x.z & 0xffff0000u);
     f[6] = __uint_as_float(x.w << 16); f[7] = __uint_as_float(x.w & 0xffff0000u);
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
 }
 
 // Window geometry of sequence n: the new slot and the number of slots [0, nvalid)
@@ -238,36 +226,46 @@ void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__
 }
 
 // One workgroup per (n, h), one thread per value channel; the (n, h) records of
-// all splits are contiguous.  The split weights 2^(m_s - max m) are formed
-// once in LDS, then every channel sums its S partial outputs independently.
+// all splits are contiguous.  Each thread folds the splits in batches of 16
+// (every load of a batch issued at once) into a running maximum, denominator
+// and output, rescaling by 2^(m_s - max m); a split with no slot in the window
+// has m = -inf and weight 0.
 template <int D>
 __global__ __launch_bounds__(D)
 void swska_decode_combine(const float *__restrict__ part, bf16_t *__restrict__ o, int *__restrict__ pos,
                           int H, int S) {
     using C = Dec<D>;
-    __shared__ float sF[kMaxSplits];
-    __shared__ float sL;
+    constexpr int B = 16;
     const int nh = blockIdx.x, d = threadIdx.x;
     const float *rec = part + (size_t)nh * S * C::PSTRIDE;
-    if (d < 64) {  // wave 0: global maximum, weights, denominator
-        float M = -INFINITY;
-        for (int s = d; s < S; s += 64) M = fmaxf(M, rec[(size_t)s * C::PSTRIDE + D]);
-        M = wave_max(M);
-        float L = 0.f;
-        for (int s = d; s < S; s += 64) {
-            const float ms = rec[(size_t)s * C::PSTRIDE + D];
-            const float f = (ms == -INFINITY) ? 0.f : exp2_fast(ms - M);  // a split with no slot in the window
-            sF[s] = f;
-            L = fmaf(f, rec[(size_t)s * C::PSTRIDE + D + 1], L);
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += B) {
+        float ms[B], ls[B], os[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const float *r = rec + (size_t)(s0 + u) * C::PSTRIDE;
+            const bool in = s0 + u < S;
+            ms[u] = in ? r[D] : -INFINITY;
+            ls[u] = in ? r[D + 1] : 0.f;
+            os[u] = in ? r[d] : 0.f;
         }
-        L = wave_sum(L);
-        if (d == 0) sL = L;
+        float mn = M;
+#pragma unroll
+        for (int u = 0; u < B; ++u) mn = fmaxf(mn, ms[u]);
+        if (mn > -INFINITY) {
+            const float f = exp2_fast(M - mn);   // exp2(-inf) = 0
+            acc *= f;
+            L *= f;
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const float w = exp2_fast(ms[u] - mn);
+                acc = fmaf(w, os[u], acc);
+                L = fmaf(w, ls[u], L);
+            }
+            M = mn;
+        }
     }
-    __syncthreads();
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) acc = fmaf(sF[s], rec[(size_t)s * C::PSTRIDE + d], acc);
-    o[(size_t)nh * D + d] = f2bf(acc / sL);
+    o[(size_t)nh * D + d] = f2bf(acc / L);   // L > 0: the new token's own slot is in the window
     if (nh % H == 0 && d == 0) pos[nh / H] += 1;
 }
 
