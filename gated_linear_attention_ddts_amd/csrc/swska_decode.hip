@@ -20,8 +20,9 @@
 // (window x dv bf16) and the key window once per sequence, for about two flops
 // per byte.  Both contractions run on the VALU in fp32.  Two kernels:
 //
-//   swska_decode_split: workgroup (n, HP heads, 256-slot split), HP = 2 when
-//       H is even (else 1), so that each key slice loaded serves HP heads.
+//   swska_decode_split: workgroup (n, HP heads, split of SPL slots), HP = 2
+//       when H is even (else 1), so that each key slice loaded serves HP
+//       heads; SPL = 1024 when that still gives 8 workgroups per CU, else 256.
 //       Each thread takes every 16th row of the split (D = 128) and one
 //       16-byte column slice of it; per group of rows it loads the key slice
 //       and the HP value slices together, sums each head's dot product over
@@ -45,7 +46,8 @@ namespace rodimus {
 
 namespace {
 
-constexpr int kSplit = 256;     // slots per value workgroup
+constexpr int kSplit = 256;      // slots per split workgroup (the workspace is sized for it)
+constexpr int kSplitLong = 1024; // slots per split workgroup when that still fills the GPU
 
 template <int D>
 struct Dec {
@@ -80,7 +82,7 @@ __device__ __forceinline__ Geo geometry(const int *pos, int n, int W) {
 // through LDS at the end.
 // Workgroups b: XCD x = b mod 8 takes the pairs (n, split) x, x + 8, ..., the
 // H / HP head groups of a pair in consecutive workgroups of that XCD.
-template <int D, int HP>
+template <int D, int HP, int SPL>
 __global__ __launch_bounds__(256)
 void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,
                         const bf16_t *__restrict__ v_new, bf16_t *__restrict__ k_cache,
@@ -95,14 +97,14 @@ void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__
     if (pair >= N * S) return;
     const int n = pair / S, s = pair % S, tid = threadIdx.x;
     const Geo g = geometry(pos, n, W);
-    const int j0 = s * kSplit;
-    const int jend = max(0, min(min(kSplit, W - j0), g.nvalid - j0));
+    const int j0 = s * SPL;
+    const int jend = max(0, min(min(SPL, W - j0), g.nvalid - j0));
     const int jn = g.jnew - j0;   // the new token's row, if this split holds it (then jn < jend)
     const int r = tid / C::VEC, c = tid % C::VEC;   // rows r, r + RP, ...; 16-byte column c
 
     // append the new token (one workgroup per cache row); this step reads
     // that row from k_new / v_new instead
-    if (jn >= 0 && jn < kSplit && tid < C::VEC) {
+    if (jn >= 0 && jn < SPL && tid < C::VEC) {
 #pragma unroll
         for (int hh = 0; hh < HP; ++hh) {
             const size_t nh = (size_t)n * H + h0 + hh;
@@ -124,7 +126,7 @@ void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__
         vn[hh] = v_new + nh * D + 8 * c;
     }
     const bf16_t *krow = k_cache + ((size_t)n * W + j0) * D + 8 * c, *kn = k_new + (size_t)n * D + 8 * c;
-    constexpr int NP = kSplit / C::RP;   // rows per thread
+    constexpr int NP = SPL / C::RP;   // rows per thread
     constexpr int G = 4;                 // rows in flight per thread
     float m[HP], lsum[HP], o[HP][8];
 #pragma unroll
@@ -286,23 +288,33 @@ size_t swska_decode_blocks(int N, int H, int window) {
     return ((size_t)N * value_splits(window) + 7) / 8 * 8 * H;
 }
 
+template <int D, int HP, int SPL>
+static void launch_split(const SkaDecArgs &a, int S, float *part, hipStream_t st) {
+    const size_t blocks = ((size_t)a.N * S + 7) / 8 * 8 * (a.H / HP);
+    hipLaunchKernelGGL((swska_decode_split<D, HP, SPL>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t *)a.q,
+                       (const bf16_t *)a.k_new, (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache,
+                       a.pos, part, a.N, a.H, a.window, S, a.scale * kLog2e);
+}
+
+// Splits of kSplitLong slots when that leaves at least 8 split workgroups per
+// CU (fewer records to combine, and each key and value stream runs longer),
+// else of kSplit slots; two heads per workgroup when H is even.
 template <int D>
 static void launch_d(const SkaDecArgs &a, hipStream_t st) {
-    const int S = value_splits(a.window);
     float *part = reinterpret_cast<float *>(a.workspace);
-    const dim3 g2((unsigned)((size_t)a.N * a.H));
-    if (a.H % 2 == 0) {
-        const dim3 g1((unsigned)(swska_decode_blocks(a.N, a.H, a.window) / 2));
-        hipLaunchKernelGGL((swska_decode_split<D, 2>), g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
-                           (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
-                           a.window, S, a.scale * kLog2e);
+    const int HP = a.H % 2 == 0 ? 2 : 1;
+    const int SL = (a.window + kSplitLong - 1) / kSplitLong;
+    const bool lng = (size_t)a.N * SL * (a.H / HP) >= 8 * 256;
+    const int S = lng ? SL : value_splits(a.window);
+    if (HP == 2) {
+        if (lng) launch_split<D, 2, kSplitLong>(a, S, part, st);
+        else launch_split<D, 2, kSplit>(a, S, part, st);
     } else {
-        const dim3 g1((unsigned)swska_decode_blocks(a.N, a.H, a.window));
-        hipLaunchKernelGGL((swska_decode_split<D, 1>), g1, dim3(256), 0, st, (const bf16_t *)a.q, (const bf16_t *)a.k_new,
-                           (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H,
-                           a.window, S, a.scale * kLog2e);
+        if (lng) launch_split<D, 1, kSplitLong>(a, S, part, st);
+        else launch_split<D, 1, kSplit>(a, S, part, st);
     }
-    hipLaunchKernelGGL(swska_decode_combine<D>, g2, dim3(D), 0, st, part, (bf16_t *)a.o, a.pos, a.H, S);
+    hipLaunchKernelGGL(swska_decode_combine<D>, dim3((unsigned)((size_t)a.N * a.H)), dim3(D), 0, st, part,
+                       (bf16_t *)a.o, a.pos, a.H, S);
 }
 
 void launch_swska_decode(const SkaDecArgs &a, hipStream_t st) {

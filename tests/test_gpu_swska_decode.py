@@ -122,3 +122,34 @@ def test_decode_N64_w4096_sampled_heads():
         e = err(host(o[n]), ref[0, :, -1])
         log(f"  n={n}: err o {e:.3e}")
         assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,H,W", [(128, 8, 4100), (512, 1, 4096)])
+def test_long_splits_against_window_oracle(N, H, W):
+    # enough (sequence, split, head group) workgroups for the 1024-slot splits
+    # (two heads per workgroup at H = 8, one at H = 1); W = 4100 leaves a
+    # ragged last split; positions from an empty window to several wraps
+    d = 128
+    log(f"swska decode long splits: N={N} H={H} W={W}")
+    kc = workloads.device_normal((N, W, d), 71 + H)
+    vc = workloads.device_normal((N, H, W, d), 72 + H)
+    x = workloads.swska_inputs(73 + H, N, H, 1, d, d)
+    qn, kn, vn = dev(x["q"])[:, :, 0].contiguous(), dev(x["k"])[:, 0].contiguous(), dev(x["v"])[:, :, 0].contiguous()
+    rng = np.random.default_rng(74 + H)
+    ts = rng.integers(0, 3 * W, size=N)
+    ts[:6] = [0, 1, 1023, 1024, W - 1, 2 * W + 5]
+    pos = torch.from_numpy(ts.astype(np.int32)).cuda()
+    o = rd.sw_ska_decode_step(qn, kn, vn, kc, vc, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(pos.cpu(), torch.from_numpy(ts.astype(np.int32) + 1))
+    for n in sorted({0, 1, 2, 3, 4, 5, N // 2, N - 1}):
+        t = int(ts[n])
+        ps = np.arange(max(0, t - W + 1), t + 1)
+        slots = torch.from_numpy(ps % W).cuda()
+        kw, vw = host(kc[n].index_select(0, slots)), host(vc[n].index_select(1, slots))
+        L = len(ps)
+        qs = np.zeros((1, H, L, d))
+        qs[0, :, -1] = host(qn[n])
+        ref = oracle.swska(qs, kw[None], vw[None], W, rows=[h * L + L - 1 for h in range(H)], nthreads=8)
+        e = err(host(o[n]), ref[0, :, -1])
+        assert e <= TOL["bf16"], (n, t, e)
