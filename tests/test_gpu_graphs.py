@@ -5,14 +5,20 @@ replay them: several decode steps, and one prefill (segment states, combine,
 output pass) or one backward (state passes, combine, gradients, fallback list
 and its counter).  Each test replays the graph several times with eager work
 and synchronisations in between, and checks every replay bit for bit against
-the same calls run eagerly."""
+the same calls run eagerly; the decode graphs are also checked against the
+fp64 oracle, replay after replay (the replays continue the same sequences).
+The last test captures a two-layer chain of both decode mixers (Rodimus then
+SW-SKA in each layer, each mixer's output feeding the next one's queries) over
+several steps into one graph and checks every output and state against the
+oracle's chain."""
 import numpy as np
 import pytest
 import torch
 
 import gated_linear_attention_ddts_amd as rd
+import oracle
 import workloads
-from tests.gpu_helpers import dev, log
+from tests.gpu_helpers import TOL, dev, err, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +49,7 @@ def test_rodimus_decode_steps_replayed_from_a_graph():
     S_eager = torch.zeros_like(S_graph)
     S_graph.zero_()
     eager_outs = [torch.empty_like(o) for o in outs]
+    S_ref = np.zeros((N, H, dk, dv))
     for rep in range(4):
         graph.replay()
         torch.cuda.synchronize()
@@ -52,6 +59,12 @@ def test_rodimus_decode_steps_replayed_from_a_graph():
         assert torch.equal(S_graph, S_eager), rep
         for i in range(K):
             assert torch.equal(outs[i], eager_outs[i]), (rep, i)
+            ro, S_ref = oracle.decode(*(sets[i][n].f64() for n in NAMES), S_ref)
+            e = err(host(outs[i]), ro)
+            assert e <= TOL["bf16"], (rep, i, e)
+        es = err(host(S_graph), S_ref)
+        log(f"  against the oracle after {K * (rep + 1)} steps: S err {es:.2e}")
+        assert es <= 1e-4, rep
 
 
 def test_swska_decode_steps_replayed_from_a_graph():
@@ -88,6 +101,7 @@ def test_swska_decode_steps_replayed_from_a_graph():
     kc_e, vc_e, pos_e = caches()
     eager_outs = [torch.empty_like(o) for o in outs]
     for rep in range(4):
+        kc_before, vc_before, pos_before = host(kc_g), host(vc_g), pos_g.cpu().numpy().copy()
         graph.replay()
         torch.cuda.synchronize()
         steps(kc_e, vc_e, pos_e, eager_outs, ws_e)
@@ -97,6 +111,36 @@ def test_swska_decode_steps_replayed_from_a_graph():
         assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), rep
         for i in range(K):
             assert torch.equal(outs[i], eager_outs[i]), (rep, i)
+        # against the oracle: each step's output is the SW-SKA row of its
+        # position over the window of keys/values the caches held, with the
+        # replay's own tokens appended in order
+        ref = _swska_decode_oracle(kc_before, vc_before, pos_before, toks, W)
+        e = err(np.stack([host(o) for o in outs]), ref)
+        log(f"  against the oracle: err {e:.2e}")
+        assert e <= TOL["bf16"], rep
+
+
+def _swska_decode_oracle(kc, vc, pos, toks, W):
+    """fp64 outputs of len(toks) SW-SKA decode steps from caches kc [N,W,d],
+    vc [N,H,W,d] (host copies) at positions pos [N]: step i appends token i at
+    position pos+i (slot (pos+i) mod W) and attends over the last W positions."""
+    kc, vc = kc.copy(), vc.copy()
+    N, H, d = vc.shape[0], vc.shape[1], vc.shape[3]
+    outs = np.zeros((len(toks), N, H, d))
+    for i, (qn, kn, vn) in enumerate(toks):
+        qh, kh, vh = host(qn), host(kn), host(vn)
+        for n in range(N):
+            t = int(pos[n]) + i
+            kc[n, t % W] = kh[n]
+            vc[n, :, t % W] = vh[n]
+            ps = list(range(max(0, t - W + 1), t + 1))
+            sl = [p % W for p in ps]
+            L = len(ps)
+            qs = np.zeros((1, H, L, d))
+            qs[0, :, -1] = qh[n]
+            r = oracle.swska(qs, kc[n][sl][None], vc[n][:, sl][None], W, rows=[h * L + L - 1 for h in range(H)])
+            outs[i, n] = r[0, :, -1]
+    return outs
 
 
 def _capture(fn):
@@ -159,3 +203,101 @@ def test_backward_replayed_from_a_graph():
         log(f"backward replay {rep}")
         for k in out_e:
             assert torch.equal(out_g[k], out_e[k]), (rep, k)
+
+
+def test_two_layer_mixer_chain_decode_graph_against_oracle():
+    """Rodimus+ decode, two layers: per layer a Rodimus decode step (global
+    recurrent mixer) then an SW-SKA decode step (local window mixer), all
+    steps of a few tokens captured into one graph.  The projections and the
+    residual stream between mixers are outside this library; in their place
+    each mixer's bf16 output is the next mixer's query (layer l's SW-SKA query
+    is its Rodimus output, layer l+1's Rodimus query is layer l's SW-SKA
+    output), so the graph's launches depend on one another in order.  Every
+    output, state and cache is checked against the oracle's chain, which
+    rounds each intermediate output to bf16 itself."""
+    N, H, d, W, K, L = 4, 4, 128, 48, 5, 2
+    rx = [workloads.decode_pool(200 + l, N, H, d, d, pool=K) for l in range(L)]   # k, v, g, theta per step
+    q0 = workloads.decode_pool(210, N, H, d, d, pool=K)                           # layer 0's queries
+    sx = [workloads.swska_inputs(220 + l, N, H, K, d, d) for l in range(L)]      # k_new, v_new per step
+    r_in = [[{n: dev(rx[l][i][n]) for n in ("k", "v", "g", "theta")} for i in range(K)] for l in range(L)]
+    q_in = [dev(q0[i]["q"]) for i in range(K)]
+    s_in = [[(dev(sx[l]["k"])[:, i].contiguous(), dev(sx[l]["v"])[:, :, i].contiguous()) for i in range(K)]
+            for l in range(L)]
+
+    def fresh_state():
+        return dict(S=[torch.zeros(N, H, d, d, device="cuda") for _ in range(L)],
+                    kc=[torch.zeros(N, W, d, dtype=torch.bfloat16, device="cuda") for _ in range(L)],
+                    vc=[torch.zeros(N, H, W, d, dtype=torch.bfloat16, device="cuda") for _ in range(L)],
+                    pos=[torch.zeros(N, dtype=torch.int32, device="cuda") for _ in range(L)],
+                    ws=[torch.empty(rd.sw_ska_decode_workspace_bytes(N, H, d, d, W), dtype=torch.uint8,
+                                    device="cuda") for _ in range(L)],
+                    o_r=[[torch.empty(N, H, d, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+                         for _ in range(L)],
+                    o_s=[[torch.empty(N, H, d, dtype=torch.bfloat16, device="cuda") for _ in range(K)]
+                         for _ in range(L)])
+
+    def run(st):
+        for i in range(K):
+            q = q_in[i]
+            for l in range(L):
+                x = r_in[l][i]
+                rd.rodimus_decode_step(q, x["k"], x["v"], x["g"], x["theta"], st["S"][l], o=st["o_r"][l][i])
+                kn, vn = s_in[l][i]
+                rd.sw_ska_decode_step(st["o_r"][l][i], kn, vn, st["kc"][l], st["vc"][l], st["pos"][l],
+                                      o=st["o_s"][l][i], workspace=st["ws"][l])
+                q = st["o_s"][l][i]
+
+    gg = fresh_state()
+    graph, _ = _capture(lambda: run(gg))   # the warm-up before capture advances gg; reset below
+
+    S_ref = [np.zeros((N, H, d, d)) for _ in range(L)]
+    K_hist = [np.zeros((N, 0, d)) for _ in range(L)]
+    V_hist = [np.zeros((N, H, 0, d)) for _ in range(L)]
+    e_st = fresh_state()
+    for rep in range(3):
+        for l in range(L):
+            gg["S"][l].zero_(); gg["kc"][l].zero_(); gg["vc"][l].zero_(); gg["pos"][l].zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if rep == 0:
+            run(e_st)                      # eager work between replays, same chain
+            torch.cuda.synchronize()
+            for l in range(L):
+                assert torch.equal(e_st["S"][l], gg["S"][l])
+                for i in range(K):
+                    assert torch.equal(e_st["o_r"][l][i], gg["o_r"][l][i])
+                    assert torch.equal(e_st["o_s"][l][i], gg["o_s"][l][i])
+            # the oracle's chain over the same K steps
+            worst = 0.0
+            for i in range(K):
+                q = q0[i]["q"].f64()
+                for l in range(L):
+                    x = rx[l][i]
+                    o_r, S_ref[l] = oracle.decode(q, *(x[n].f64() for n in ("k", "v", "g", "theta")), S_ref[l])
+                    o_r_bf = workloads.round_to(o_r, "bf16").astype(np.float64)
+                    K_hist[l] = np.concatenate([K_hist[l], sx[l]["k"].f64()[:, i:i + 1]], axis=1)
+                    V_hist[l] = np.concatenate([V_hist[l], sx[l]["v"].f64()[:, :, i:i + 1]], axis=2)
+                    T = i + 1
+                    qs = np.zeros((N, H, T, d))
+                    qs[:, :, -1] = o_r_bf
+                    rows = [(n * H + h) * T + T - 1 for n in range(N) for h in range(H)]
+                    o_s = oracle.swska(qs, K_hist[l], V_hist[l], W, rows=rows)[:, :, -1]
+                    e1 = err(host(gg["o_r"][l][i]), o_r)
+                    e2 = err(host(gg["o_s"][l][i]), o_s)
+                    worst = max(worst, e1, e2)
+                    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"], (i, l, e1, e2)
+                    q = workloads.round_to(o_s, "bf16").astype(np.float64)
+            for l in range(L):
+                es = err(host(gg["S"][l]), S_ref[l])
+                assert es <= 1e-4, (l, es)
+                assert torch.equal(gg["pos"][l].cpu(), torch.full((N,), K, dtype=torch.int32))
+            log(f"two-layer chain: worst output err {worst:.2e} against the oracle")
+            ref_o = [[host(gg["o_r"][l][i]) for i in range(K)] for l in range(L)]
+            ref_s = [[host(gg["o_s"][l][i]) for i in range(K)] for l in range(L)]
+        else:
+            # replays from the same zero state repeat the first replay bit for bit
+            for l in range(L):
+                for i in range(K):
+                    assert np.array_equal(host(gg["o_r"][l][i]), ref_o[l][i]), (rep, l, i)
+                    assert np.array_equal(host(gg["o_s"][l][i]), ref_s[l][i]), (rep, l, i)
+            log(f"two-layer chain: replay {rep} repeats replay 0")
