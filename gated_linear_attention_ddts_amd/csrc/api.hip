@@ -48,6 +48,18 @@ const char *rodimus_status_string(int status) {
     }
 }
 
+// Every launch of a prefill stays below HIP's 2^32 work-items.
+static bool scan_launch_fits(const ScanPlan &plan, int B, int H, int T, int chunk) {
+    const long long BH = (long long)B * H;
+    const uint64_t items = plan.mfma ? scan_mfma_launch_items(BH, T, chunk) : scan_generic_launch_items(BH);
+    return items < kMaxLaunchItems;
+}
+
+static bool scan_bwd_launch_fits(bool mfma, int B, int H, int T) {
+    const long long BH = (long long)B * H;
+    return (mfma ? scan_bwd_mfma_launch_items(BH, T) : scan_bwd_launch_items(BH, T)) < kMaxLaunchItems;
+}
+
 static bool scan_sizes_ok(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     if (B < 0 || H < 0 || T < 0) return false;
     if (!ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype)) return false;
@@ -86,6 +98,7 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(o))
         return RODIMUS_ERR_INVALID_ARG;
     ScanPlan plan = plan_scan(B, H, T, dk, dv, chunk, dtype);
+    if (!scan_launch_fits(plan, B, H, T, chunk)) return RODIMUS_ERR_INVALID_ARG;
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return RODIMUS_ERR_INVALID_ARG;
     ScanArgs a{q, k, v, g, tau, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, workspace,
@@ -125,6 +138,7 @@ int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, con
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(o))
         return RODIMUS_ERR_INVALID_ARG;
     ScanPlan plan = plan_scan(N, H, max_seqlen, dk, dv, chunk, dtype);
+    if (!scan_launch_fits(plan, N, H, max_seqlen, chunk)) return RODIMUS_ERR_INVALID_ARG;
     const size_t need = plan.workspace_bytes + seq_order_bytes(N);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return RODIMUS_ERR_INVALID_ARG;
     ScanArgs a{q, k, v, g, tau, S0, o, S_T, N, H, max_seqlen, dk, dv, chunk, dtype, workspace,
@@ -168,6 +182,7 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
         !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
         return RODIMUS_ERR_INVALID_ARG;
     const bool mfma = scan_bwd_mfma_supported(T, dk, dv, dtype);
+    if (!scan_bwd_launch_fits(mfma, B, H, T)) return RODIMUS_ERR_INVALID_ARG;
     const size_t need = mfma ? scan_bwd_mfma_workspace(B, H, T) : scan_bwd_workspace(B, H, T, dk, dv);
     if (workspace == nullptr || workspace_bytes < need) return RODIMUS_ERR_INVALID_ARG;
     ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, B, H, T, dk, dv, dtype,
@@ -206,6 +221,7 @@ int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, co
         !ok_ptr(dq) || !ok_ptr(dk_) || !ok_ptr(dv_) || !ok_ptr(dg) || !ok_ptr(dtau))
         return RODIMUS_ERR_INVALID_ARG;
     const bool mfma = scan_bwd_mfma_supported(max_seqlen, dk, dv, dtype);
+    if (!scan_bwd_launch_fits(mfma, N, H, max_seqlen)) return RODIMUS_ERR_INVALID_ARG;
     const size_t base = mfma ? scan_bwd_mfma_workspace(N, H, max_seqlen) : scan_bwd_workspace(N, H, max_seqlen, dk, dv);
     if (workspace == nullptr || workspace_bytes < base + seq_order_bytes(N)) return RODIMUS_ERR_INVALID_ARG;
     ScanBwdArgs a{q, k, v, g, tau, S0, dO, dS_T, dq, dk_, dv_, dg, dtau, dS0, N, H, max_seqlen, dk, dv, dtype,
@@ -226,7 +242,8 @@ int rodimus_decode_step(const void *q, const void *k, const void *v, const void 
                         int N, int H, int dk, int dv, int dtype, void *stream) {
     if (N < 0 || H < 0 || !ok_head_dim(dk) || !ok_head_dim(dv) || !ok_dtype(dtype))
         return RODIMUS_ERR_INVALID_ARG;
-    if ((long long)N * H > (1LL << 30)) return RODIMUS_ERR_INVALID_ARG;
+    // one workgroup of up to 256 threads per (sequence, head): N*H < 2^24
+    if (decode_launch_items((long long)N * H) >= kMaxLaunchItems) return RODIMUS_ERR_INVALID_ARG;
     if (N == 0 || H == 0) return RODIMUS_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(g) || !ok_ptr(tau) || !ok_ptr(S_in) ||
         !ok_ptr(S_out) || !ok_ptr(o))
@@ -249,6 +266,7 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
     if (!(scale > 0.f) || !(scale < 3.0e38f)) return RODIMUS_ERR_INVALID_ARG;
     if ((long long)B * H * T * (dk > dv ? dk : dv) > (1LL << 46)) return RODIMUS_ERR_INVALID_ARG;
     if (!swska_supported(T, dk, dv, dtype)) return RODIMUS_ERR_UNSUPPORTED;
+    if (swska_launch_items((long long)B * H, T, dk) >= kMaxLaunchItems) return RODIMUS_ERR_INVALID_ARG;
     if (B == 0 || H == 0 || T == 0) return RODIMUS_OK;
     if (!ok_ptr(q) || !ok_ptr(k_shared) || !ok_ptr(v) || !ok_ptr(o)) return RODIMUS_ERR_INVALID_ARG;
     SkaArgs a{q, k_shared, v, o, B, H, T, dk, dv, window, scale, dtype};

@@ -150,6 +150,9 @@ static void launch_typed(const DecodeArgs &a, hipStream_t st) {
                        (const Tin *)a.tau, a.S_in, a.S_out, (Tin *)a.o, a.dk, a.dv);
 }
 
+// One workgroup per (sequence, head) of at most 256 threads.
+uint64_t decode_launch_items(long long NH) { return (uint64_t)NH * 256; }
+
 void launch_decode_step(const DecodeArgs &a, hipStream_t st) {
     if (a.dtype == 0) launch_typed<float>(a, st);
     else launch_typed<bf16_t>(a, st);

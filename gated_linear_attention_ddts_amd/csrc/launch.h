@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace rodimus {
 
@@ -77,6 +78,17 @@ struct ScanPlan {
     size_t workspace_bytes;
 };
 ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+// Work-items (workgroups x threads, in x) of the largest launch a call makes.
+// HIP rejects a launch of 2^32 work-items or more, so the C ABI refuses such
+// sizes with RODIMUS_ERR_INVALID_ARG before launching anything.
+constexpr uint64_t kMaxLaunchItems = 1ull << 32;
+uint64_t scan_mfma_launch_items(long long BH, int T, int chunk);
+uint64_t scan_generic_launch_items(long long BH);
+uint64_t scan_bwd_mfma_launch_items(long long BH, int T);
+uint64_t scan_bwd_launch_items(long long BH, int T);
+uint64_t decode_launch_items(long long NH);
+uint64_t swska_launch_items(long long BH, int T, int dk);
 
 void launch_decode_step(const DecodeArgs &a, hipStream_t st);
 void launch_scan_generic(const ScanArgs &a, hipStream_t st);

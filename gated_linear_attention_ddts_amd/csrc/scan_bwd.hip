@@ -159,6 +159,11 @@ size_t scan_bwd_workspace(int B, int H, int T, int dk, int dv) {
     return 2 * (size_t)B * H * scan_bwd_chunks(T) * dk * dv * sizeof(float);
 }
 
+uint64_t scan_bwd_launch_items(long long BH, int T) {
+    const uint64_t a = (uint64_t)BH * 256, b = (uint64_t)BH * scan_bwd_chunks(T) * 256;
+    return a > b ? a : b;
+}
+
 template <typename Tin>
 static void launch_bwd_t(const ScanBwdArgs &a, hipStream_t st) {
     const int BH = a.B * a.H, nck = scan_bwd_chunks(a.T);

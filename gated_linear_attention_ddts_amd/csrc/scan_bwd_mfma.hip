@@ -44,6 +44,8 @@
 //                       epilogue in the producer-lane layout.  Two workgroups
 //                       per CU; the two halves of an interval run on one XCD.
 //   bwd_fallback_kernel the listed wide-span halves, with the exact routine.
+#include <algorithm>
+
 #include "launch.h"
 #include "mfma_common.h"
 #include "scan_bwd_body.h"
@@ -802,6 +804,15 @@ bool scan_bwd_mfma_supported(int T, int dk, int dv, int dtype) {
 size_t scan_bwd_mfma_workspace(int B, int H, int T) {
     if (B <= 0 || H <= 0 || T <= 0) return 0;
     return plan((long long)B * H, T).bytes;
+}
+
+uint64_t scan_bwd_mfma_launch_items(long long BH, int T) {
+    if (BH <= 0 || T <= 0) return 0;
+    const Plan q = plan(BH, T);
+    uint64_t m = (uint64_t)2 * BH * q.nseg * 256;                               // state passes
+    if (q.nseg > 1) m = std::max<uint64_t>(m, (uint64_t)BH * kD * kD);          // combine
+    m = std::max<uint64_t>(m, ((uint64_t)BH * q.nck + 7) / 8 * 16 * 256);       // gradients
+    return std::max<uint64_t>(m, (uint64_t)kSlowWG * 256);                      // fallback
 }
 
 void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {

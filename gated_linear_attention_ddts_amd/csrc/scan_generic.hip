@@ -182,6 +182,8 @@ static void launch_typed(const ScanArgs &a, hipStream_t st) {
     }
 }
 
+uint64_t scan_generic_launch_items(long long BH) { return (uint64_t)BH * 64; }
+
 void launch_scan_generic(const ScanArgs &a, hipStream_t st) {
     if (a.dtype == 0) launch_typed<float>(a, st);
     else launch_typed<bf16_t>(a, st);

@@ -49,6 +49,8 @@
 // the channels of Qt/Kh and the tokens of Kb^T/V^T in the matching order
 // (blocks of 4 permuted as 0,2,1,3 inside each 16), so every operand read is
 // one 16-byte ds_read.
+#include <algorithm>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -316,6 +318,10 @@ void scan_full_kernel(Params p) {
                     if (__hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= cbar_target) break;
                     __builtin_amdgcn_s_sleep(1);
                 }
+                // a wait that gave up leaves score tiles that may be stale: this
+                // chunk's outputs are then written as NaN, never as silent garbage
+                const bool stale =
+                    __hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < cbar_target;
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
                 // o^T tiles: 32 value channels (this wave's) x 32 tokens (32It..).  Same
                 // fragments as o = Qt S + A V with the operands swapped, so that a
@@ -332,11 +338,15 @@ void scan_full_kernel(Params p) {
                     const int t = t0 + 32 * It + l32;
                     if (t < t_end) {
                         bf16_t *op = p.o + (rowbase + t) * kD + 32 * cw + 4 * h;
+                        // (the NaN is written as a bit pattern: this file is built
+                        // without NaN semantics for arithmetic)
+                        constexpr uint32_t kNaN2 = 0x7fc07fc0u;
 #pragma unroll
                         for (int a4 = 0; a4 < 4; ++a4)
                             *reinterpret_cast<uint2 *>(op + 8 * a4) =
-                                make_uint2(pack2(acc[4 * a4 + 0], acc[4 * a4 + 1]),
-                                           pack2(acc[4 * a4 + 2], acc[4 * a4 + 3]));
+                                stale ? make_uint2(kNaN2, kNaN2)
+                                      : make_uint2(pack2(acc[4 * a4 + 0], acc[4 * a4 + 1]),
+                                                   pack2(acc[4 * a4 + 2], acc[4 * a4 + 3]));
                     }
                 }
                 // state: S <- diag(gamma) S + Kb^T V
@@ -546,6 +556,18 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     pl.segments = q.G;
     if (q.G > 1) pl.workspace_bytes = (size_t)(q.G - 1) * q.P * BH * (kD * kD + kD) * sizeof(float);
     return pl;
+}
+
+uint64_t scan_mfma_launch_items(long long BH, int T, int chunk) {
+    const long long nchunks = ((long long)T + chunk - 1) / chunk;
+    if (BH <= 0 || nchunks <= 0) return 0;
+    const Plan3 q = plan3(BH, nchunks);
+    uint64_t m = (uint64_t)q.G * BH * 512;                                   // output pass
+    if (q.G > 1) {
+        m = std::max<uint64_t>(m, (uint64_t)(q.G - 1) * q.P * BH * 256);     // state pass
+        m = std::max<uint64_t>(m, ((uint64_t)BH * kD * kD / 4 + 255) / 256 * 256);  // combine
+    }
+    return m;
 }
 
 void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {

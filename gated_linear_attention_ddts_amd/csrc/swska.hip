@@ -295,6 +295,11 @@ bool swska_supported(int T, int dk, int dv, int dtype) {
     return dtype == 1 && dk == dv && (dk == 128 || dk == 64) && (long long)T * dk * 2 < (1LL << 31);
 }
 
+uint64_t swska_launch_items(long long BH, int T, int dk) {
+    if (dk == 128) return (uint64_t)BH * (((uint64_t)T + 255) / 256) * 512;
+    return (uint64_t)BH * (((uint64_t)T + 127) / 128) * 256;
+}
+
 void launch_swska(const SkaArgs &a, hipStream_t st) {
     const int BH = a.B * a.H;
     const float sl2e = a.scale * kLog2e;

@@ -74,14 +74,12 @@ __device__ __forceinline__ Geo geometry(const int *pos, int n, int W) {
 }
 
 // Workgroups b: XCD x = b mod 8 takes the pairs (n, split) x, x + 8, ..., the
-// H heads of a pair in consecutive workgroups of that XCD.  Thread (r, c) takes
-// the split's rows r, r + RP, ... and their 16-byte column slice c: per group
-// of G rows it loads the key and value slices together, sums the key slice's
-// dot product with q over the VEC lanes of the row, and folds the rows into a
-// running maximum, sum and output (base 2).  The RP row threads are merged
-// through LDS at the end.
-// Workgroups b: XCD x = b mod 8 takes the pairs (n, split) x, x + 8, ..., the
-// H / HP head groups of a pair in consecutive workgroups of that XCD.
+// H / HP head groups of a pair in consecutive workgroups of that XCD.  Thread
+// (r, c) takes the split's rows r, r + RP, ... and their 16-byte column slice
+// c: per group of G rows it loads the key slice and the HP heads' value slices
+// together, sums the key slice's dot product with each head's q over the VEC
+// lanes of the row, and folds the rows into a running maximum, sum and output
+// per head (base 2).  The RP row threads are merged through LDS at the end.
 template <int D, int HP, int SPL>
 __global__ __launch_bounds__(256)
 void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,

@@ -49,9 +49,17 @@
  *    even.
  *  - stream is a hipStream_t (NULL = the null stream).  Every call only
  *    enqueues work; nothing is synchronised inside the library.
+ *  - ABI types: `int dtype` carries a rodimus_dtype value and `void *stream` a
+ *    hipStream_t.  Both are passed as plain C types so that this header needs
+ *    no HIP header and binds from any FFI; they are the same width and
+ *    calling convention as the enum and the pointer typedef they stand for.
  *  - Arguments are validated before any HIP call.  On a non-OK return nothing
  *    has been launched, except RODIMUS_ERR_HIP (a launch error reported by the
  *    runtime).  No exception crosses the ABI.
+ *  - Launch size: HIP refuses a launch of 2^32 work-items or more.  Every
+ *    entry point computes the largest launch its arguments need and returns
+ *    RODIMUS_ERR_INVALID_ARG (nothing launched) if it would reach that limit;
+ *    the limits are stated per entry point below.
  *  - Inputs must be finite, except tau = -inf, which is defined (a = beta = 1).
  */
 #ifndef RODIMUS_H
@@ -92,13 +100,23 @@ size_t rodimus_scan_prefill_workspace_bytes(int B, int H, int T, int dk, int dv,
  *   S_T          : [B, H, dk, dv] float, receives the state after token T-1;
  *                  NULL skips it.  May not alias S0.
  *   chunk        : C in {16, 32, 64}, or 0 for 64.  The result does not depend
- *                  on C beyond rounding.
+ *                  on C beyond rounding.  Paths: bf16 with dk = dv = 128 and
+ *                  C in {32, 64} runs on the matrix cores; every other
+ *                  combination (fp32, other head sizes, and C = 16 at any
+ *                  dtype) runs the fp32 vector-unit chunked kernel, one
+ *                  64-lane wave per (b,h) and 64 value columns, which at the
+ *                  1.6B shape is an order of magnitude slower.  C = 16 exists
+ *                  for small head sizes and parity checks, not for speed.
  *   workspace    : device scratch of at least
  *                  rodimus_scan_prefill_workspace_bytes(...) bytes (may be
  *                  NULL when that is 0).  Its contents are overwritten.
  *
  * Sizes: B, H, T >= 0 (T = 0 copies S0, or zeros, to S_T); dk, dv multiples
- * of 16 in [16, 128].  A too-small workspace gives RODIMUS_ERR_INVALID_ARG.
+ * of 16 in [16, 128]; B*H <= 2^30 and B*H*T*max(dk,dv) <= 2^46.  Launch size:
+ * the matrix-core path launches one 512-thread workgroup per (b,h) and
+ * segment (B*H < 2^23 once B*H >= 256), the vector path one 64-thread wave per
+ * (b,h) (B*H < 2^26).  A too-small workspace or a size beyond these gives
+ * RODIMUS_ERR_INVALID_ARG.
  */
 int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void *g,
                          const void *tau, const float *S0, void *o, float *S_T,
@@ -155,6 +173,9 @@ int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, con
  *   grad_S0 : [B, H, dk, dv], or NULL (not returned)
  * S0 NULL means zeros, as in the forward.  Supported: fp32 or bf16 inputs,
  * dk and dv multiples of 16 up to 128 (else RODIMUS_ERR_INVALID_ARG).
+ * Launch size: the matrix-core path launches 8 work-items per token-head in
+ * its gradient kernel (B*H*T < 2^29), the vector path 8 per token-head too
+ * (256 threads per 32-token chunk); beyond that RODIMUS_ERR_INVALID_ARG.
  * Two paths, chosen from the arguments:
  *   - bf16 with dk = dv = 128: matrix cores (bf16 operands, fp32
  *     accumulation, bf16 state checkpoints every 64 tokens); same accuracy
@@ -224,7 +245,9 @@ int rodimus_scan_backward_varlen(const void *q, const void *k, const void *v, co
  *   S_in, S_out  : [N, H, dk, dv] float; S_out may equal S_in (in place) but
  *                  must not partially overlap it.
  *
- * Sizes: N, H >= 0; dk, dv multiples of 16 in [16, 128].
+ * Sizes: N, H >= 0; dk, dv multiples of 16 in [16, 128]; N*H < 2^24 (one
+ * workgroup of up to 256 threads per sequence and head), else
+ * RODIMUS_ERR_INVALID_ARG.
  */
 int rodimus_decode_step(const void *q, const void *k, const void *v, const void *g,
                         const void *tau, const float *S_in, float *S_out, void *o,
@@ -244,7 +267,10 @@ int rodimus_decode_step(const void *q, const void *k, const void *v, const void 
  * No rotary embedding is applied: pass rotated q and k.  Supported:
  * RODIMUS_BF16 with dk = dv = 128 or dk = dv = 64, and T * dk * 2 < 2^31
  * (T <= 8388607 at dk = 128, T <= 16777215 at dk = 64); other combinations
- * return RODIMUS_ERR_UNSUPPORTED.  B, H, T >= 0.
+ * return RODIMUS_ERR_UNSUPPORTED.  B, H, T >= 0.  Launch size: one workgroup
+ * per (b,h) and block of 256 queries (512 threads; at dk = 64, 128 queries
+ * and 256 threads), i.e. 2 work-items per query row: B*H*T below about
+ * 2^31, else RODIMUS_ERR_INVALID_ARG.
  */
 int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
                 int B, int H, int T, int dk, int dv, int window, float scale, int dtype,
@@ -271,11 +297,18 @@ int sw_ska_attn(const void *q, const void *k_shared, const void *v, void *o,
  * in stream order.  Slots that hold no position of the window (t + 1 <
  * window) are never read.  A negative pos is treated as 0.
  *
+ * Work split: the window is cut into splits of 256 slots, or of 1024 slots
+ * when that still leaves at least 8 split workgroups per compute unit; a
+ * split workgroup (256 threads) serves two heads when H is even, else one,
+ * and a second kernel merges the splits' partial softmax results.
+ *
  * Supported: RODIMUS_BF16 with dk = dv = 128 or 64 (else
  * RODIMUS_ERR_UNSUPPORTED); scale finite and > 0; 1 <= window <= 524288;
- * N * H < 2^24 and N * ceil(window / 256) * H below about 2^24 (one
- * workgroup per sequence, head and 256-slot split; a launch stays below 2^32
- * work-items) (else RODIMUS_ERR_INVALID_ARG).  All buffers
+ * N * H < 2^24 and N * ceil(window / 256) * H below about 2^24 (else
+ * RODIMUS_ERR_INVALID_ARG).  The second limit is a conservative bound: it
+ * counts 256-slot splits and one head per workgroup, the most workgroups of
+ * 256 threads the step can launch, so every launch stays below 2^32
+ * work-items.  All buffers
  * are caller-owned device memory, 16-byte aligned (pos: 4-byte aligned).
  * `workspace` holds per-split partial results: at least
  * sw_ska_decode_workspace_bytes(N, H, dk, dv, window, dtype) bytes, else

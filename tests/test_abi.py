@@ -292,3 +292,46 @@ def test_scan_backward_varlen_empty_and_workspace():
                 == rd.rodimus_scan_backward_workspace_bytes(N, H, L, d, d, dt) + _order_bytes(N))
     need = rd.rodimus_scan_backward_varlen_workspace_bytes(3, 2, 64, 128, 128, rd.BF16)
     assert bwd_varlen(ws_bytes=need - 4) == rd.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- launch sizes
+# HIP refuses a launch of 2^32 work-items or more.  Each entry point computes
+# its largest launch before doing anything and returns INVALID_ARG (instead of
+# launching and reporting ERR_HIP).  A huge workspace is passed so that only the
+# launch-size rule can reject these calls; no pointer is ever dereferenced.
+HUGE_WS = 1 << 62
+
+
+def test_prefill_rejects_a_grid_beyond_hip_limits():
+    # matrix-core path: one 512-thread workgroup per (b,h) once B*H >= 256
+    assert scan(B=1 << 13, H=1 << 10, T=64, dk=128, dv=128, ws=FAKE, ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+    assert scan(B=1 << 12, H=1 << 11, T=64, dk=128, dv=128, chunk=32, ws=FAKE,
+                ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+    # vector path (fp32): one 64-thread wave per (b,h)
+    assert scan(B=1 << 16, H=1 << 10, T=1, dk=16, dv=16, dtype=rd.F32, ws=FAKE,
+                ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+    # the packed form applies the same plan
+    assert varlen(N=1 << 13, H=1 << 10, total=1 << 13, maxlen=64, ws=FAKE,
+                  ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+
+
+def test_backward_rejects_a_grid_beyond_hip_limits():
+    # matrix-core gradient kernel: 8 work-items per token-head
+    assert bwd(B=1, H=1 << 10, T=1 << 19, dk=128, dv=128, ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+    # vector path: 256 threads per 32-token chunk of every (b,h)
+    assert bwd(B=1, H=1 << 10, T=1 << 19, dk=16, dv=16, dtype=rd.F32, ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+    assert bwd_varlen(N=1 << 10, H=1, total=1 << 19, maxlen=1 << 19, ws_bytes=HUGE_WS) == rd.ERR_INVALID_ARG
+
+
+def test_decode_rejects_a_grid_beyond_hip_limits():
+    # one workgroup of up to 256 threads per (sequence, head): N*H < 2^24
+    assert decode(N=1 << 12, H=1 << 12) == rd.ERR_INVALID_ARG
+    assert decode(N=1 << 24, H=1) == rd.ERR_INVALID_ARG
+    assert decode(N=1 << 12, H=1 << 12, dk=128, dv=128) == rd.ERR_INVALID_ARG
+
+
+def test_swska_rejects_a_grid_beyond_hip_limits():
+    # one 512-thread workgroup per (b,h) and 256 query rows
+    assert ska(B=1, H=1 << 10, T=1 << 21) == rd.ERR_INVALID_ARG
+    # d = 64: 256 threads per 128 query rows
+    assert ska(B=1, H=1 << 10, T=1 << 21, dk=64, dv=64) == rd.ERR_INVALID_ARG
