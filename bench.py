@@ -119,20 +119,53 @@ def _dev(t):
     return torch.from_numpy(np.ascontiguousarray(t.storage().view(np.int16))).cuda().view(torch.bfloat16)
 
 
+LAST_TIMING = {}
+
+
 def _time(fn, steps, warmup):
-    """Average GPU time (ms) of fn() over `steps` calls, HIP events on torch's stream."""
+    """Average GPU time (ms) of fn() over `steps` back-to-back calls, HIP events
+    on torch's stream (the stream the library launches on).  An event is also
+    recorded between consecutive calls, so the per-call median and minimum are
+    kept in LAST_TIMING beside the mean."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    LAST_TIMING.clear()
+    LAST_TIMING.update(mean=mean, median=float(np.median(per)), min=float(np.min(per)))
+    return mean
+
+
+def _time_cold(fn, steps, flush_bytes=512 << 20):
+    """Per-call GPU time (ms) with the caches cold: before each call a
+    `flush_bytes` buffer (twice the 256 MB Infinity Cache) is written, and only
+    the call itself sits between the two events.  Returns (median, min)."""
+    import torch
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    per = []
+    for i in range(steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    del flush
+    return float(np.median(per)), float(np.min(per))
+
+
+def _timing_fields(ms_scale=1.0, prefix="ms"):
+    t = dict(LAST_TIMING)
+    return {f"{prefix}_median": round(t["median"] * ms_scale, 4), f"{prefix}_min": round(t["min"] * ms_scale, 4)}
 
 
 def prefill_bytes(B, H, T, dk, dv):
@@ -144,7 +177,7 @@ def prefill_flops(B, H, T, dk, dv, C):
     return B * H * T * (4 * dk * dv + (C + 1) * (dk + dv))
 
 
-def bench_prefill(cfg, steps, warmup):
+def bench_prefill(cfg, steps, warmup, cold=True):
     import torch
     import gated_linear_attention_ddts_amd as rd
     import workloads
@@ -163,11 +196,17 @@ def bench_prefill(cfg, steps, warmup):
                                 workspace=ws)
 
     ms = _time(step, steps, warmup)
+    tf = _timing_fields()
+    cold_med, cold_min = _time_cold(step, max(5, steps // 2)) if cold else (None, None)
     nbytes = prefill_bytes(B, H, T, dk, dv)
     flops = prefill_flops(B, H, T, dk, dv, C)
-    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
-                gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
-                workspace_bytes=nws)
+    r = dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
+             gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
+             workspace_bytes=nws, **tf)
+    if cold:
+        r.update(ms_cold_median=cold_med, ms_cold_min=cold_min,
+                 gbs_cold=nbytes / (cold_med * 1e-3) / 1e9)
+    return r
 
 
 def bench_varlen(cfg, steps, warmup):
@@ -194,7 +233,7 @@ def bench_varlen(cfg, steps, warmup):
     # per token-head q, k, g, tau, v in and o out (bf16), plus every fp32 S_T
     nbytes = H * total * (4 * dk * 2 + dv * 2 + dv * 2) + N * H * dk * dv * 4
     return dict(ms=ms, tokens_per_s=total / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                sequences=N, max_len=maxlen, min_len=int(L.min()))
+                sequences=N, max_len=maxlen, min_len=int(L.min()), **_timing_fields())
 
 
 def bench_backward_varlen(cfg, steps, warmup):
@@ -224,7 +263,8 @@ def bench_backward_varlen(cfg, steps, warmup):
     # per token-head the same bytes as the batched backward, plus every fp32 dS0
     nbytes = backward_bytes(1, H, total, dk, dv) - H * dk * dv * 4 + N * H * dk * dv * 4
     return dict(ms=ms, tokens_per_s=total / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                sequences=N, max_len=maxlen, min_len=int(L.min()), workspace_bytes=ws.numel())
+                sequences=N, max_len=maxlen, min_len=int(L.min()), workspace_bytes=ws.numel(),
+                **_timing_fields())
 
 
 def backward_bytes(B, H, T, dk, dv):
@@ -261,14 +301,22 @@ def bench_backward(cfg, steps, warmup):
     flops = backward_flops(B, H, T, dk, dv)
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, flops=flops,
                 gbs=nbytes / (ms * 1e-3) / 1e9, tflops=flops / (ms * 1e-3) / 1e12,
-                workspace_bytes=ws.numel())
+                workspace_bytes=ws.numel(), **_timing_fields())
 
 
 def decode_bytes(N, H, dk, dv):
     return N * H * (2 * dk * dv * 4 + (4 * dk + dv) * 2 + dv * 2)
 
 
-def bench_decode(cfg, steps, warmup):
+def bench_decode(cfg, steps, warmup, big_n=1024):
+    """Decode steps on resident states, three ways:
+    * in place, N = 256: the workload as specified; its 268 MB state is about
+      the size of the 256 MB Infinity Cache, so part of each step is served
+      from that cache (cache-assisted, labelled so);
+    * ping-pong, N = 256: S_in and S_out alternate between two buffers, so each
+      step reads one 268 MB state and writes another (a 537 MB working set):
+      the HBM-true rate of the same step, and the roofline figure;
+    * in place, N = `big_n`: a 1.07 GB state, far larger than the cache."""
     import torch
     import gated_linear_attention_ddts_amd as rd
     import workloads
@@ -285,11 +333,9 @@ def bench_decode(cfg, steps, warmup):
         rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], S, o=o)
 
     ms = _time(step, steps, warmup)
+    tf = _timing_fields(1e3, "us_per_step")
     ms_graph = _graph_time(step, len(dsets), 8)
 
-    # ping-pong: S_in and S_out alternate between two buffers, so the step
-    # reads one 268 MB state and writes another (a 537 MB working set, twice the
-    # 256 MB Infinity Cache) instead of updating one in place
     S2 = torch.zeros_like(S)
 
     def step_pp():
@@ -299,10 +345,31 @@ def bench_decode(cfg, steps, warmup):
         rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], a, b, o=o)
 
     ms_pp = _time(step_pp, steps, warmup)
+    tf_pp = _timing_fields(1e3, "us_per_step")
+    del S2
+
+    # a batch whose state is four times the cache: inputs replicated from the pool
+    rep = big_n // N
+    bsets = [{n: t.repeat(rep, *([1] * (t.dim() - 1))).contiguous() for n, t in s.items()} for s in dsets]
+    Sb = torch.zeros(big_n, H, dk, dv, dtype=torch.float32, device="cuda")
+    ob = torch.empty(big_n, H, dv, dtype=torch.bfloat16, device="cuda")
+
+    def step_big():
+        s = bsets[state["s"] % len(bsets)]
+        state["s"] += 1
+        rd.rodimus_decode_step(s["q"], s["k"], s["v"], s["g"], s["theta"], Sb, o=ob)
+
+    ms_big = _time(step_big, max(50, steps // 4), warmup)
+    tf_big = _timing_fields(1e3, "us_per_step")
+    del Sb, bsets
     nbytes = decode_bytes(N, H, dk, dv)
+    nbig = decode_bytes(big_n, H, dk, dv)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
                 gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3,
-                us_per_step_pingpong=ms_pp * 1e3, gbs_pingpong=nbytes / (ms_pp * 1e-3) / 1e9)
+                timing=tf, us_per_step_pingpong=ms_pp * 1e3, gbs_pingpong=nbytes / (ms_pp * 1e-3) / 1e9,
+                timing_pingpong=tf_pp, tokens_per_s_pingpong=N / (ms_pp * 1e-3),
+                big_n=big_n, us_per_step_big=ms_big * 1e3, bytes_big=nbig,
+                gbs_big=nbig / (ms_big * 1e-3) / 1e9, timing_big=tf_big)
 
 
 def _graph_time(step, n_capture, replays):
@@ -352,7 +419,7 @@ def bench_swska(cfg, steps, warmup):
     flops = B * H * swska_pairs(T, w) * 2 * (dk + dv)
     nbytes = (B * H * T * (dk + 2 * dv) + B * T * dk) * 2
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), flops=flops,
-                tflops=flops / (ms * 1e-3) / 1e12, bytes=nbytes)
+                tflops=flops / (ms * 1e-3) / 1e12, bytes=nbytes, **_timing_fields())
 
 
 def swska_decode_bytes(N, H, dk, dv, window):
@@ -387,10 +454,56 @@ def bench_swska_decode(cfg, steps, warmup):
         rd.sw_ska_decode_step(qn, kn, vn, kc, vc, pos, o=o, workspace=ws)
 
     ms = _time(step, steps, warmup)
+    tf = _timing_fields(1e3, "us_per_step")
     ms_graph = _graph_time(step, len(toks), 4)
     nbytes = swska_decode_bytes(N, H, dk, dv, W)
     return dict(ms=ms, us_per_step=ms * 1e3, tokens_per_s=N / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3)
+                gbs=nbytes / (ms * 1e-3) / 1e9, steps=steps, us_per_step_graph=ms_graph * 1e3, **tf)
+
+
+def bench_mixer_chain(N=16, H=16, d=128, window=4096, layers=2, pos0=8192, steps=200, warmup=10, seed=8):
+    """Rodimus+ decode at a small batch: per token, in each of `layers` layers,
+    a Rodimus decode step then an SW-SKA decode step over a full window cache,
+    each mixer's output being the next one's query (the projections between
+    them are outside this library).  Timed eagerly (one launch after another)
+    and replayed from one HIP graph holding 8 tokens' launches."""
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    pool = 8
+    rsets = [workloads.decode_pool(seed * 10 + l, N, H, d, d, pool=pool) for l in range(layers)]
+    r_in = [[{n: _dev(x[n]) for n in NAMES} for x in rsets[l]] for l in range(layers)]
+    sx = [workloads.swska_inputs(seed * 10 + 5 + l, N, H, pool, d, d) for l in range(layers)]
+    s_in = [[(_dev(sx[l]["k"])[:, i].contiguous(), _dev(sx[l]["v"])[:, :, i].contiguous()) for i in range(pool)]
+            for l in range(layers)]
+    S = [torch.zeros(N, H, d, d, device="cuda") for _ in range(layers)]
+    kc = [workloads.device_normal((N, window, d), seed * 100 + l) for l in range(layers)]
+    vc = [workloads.device_normal((N, H, window, d), seed * 100 + 50 + l) for l in range(layers)]
+    pos = [torch.full((N,), pos0, dtype=torch.int32, device="cuda") for _ in range(layers)]
+    ws = [torch.empty(rd.sw_ska_decode_workspace_bytes(N, H, d, d, window), dtype=torch.uint8, device="cuda")
+          for _ in range(layers)]
+    o_r = [torch.empty(N, H, d, dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    o_s = [torch.empty(N, H, d, dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    state = {"s": 0}
+
+    def step():
+        i = state["s"] % pool
+        state["s"] += 1
+        q = r_in[0][i]["q"]
+        for l in range(layers):
+            x = r_in[l][i]
+            rd.rodimus_decode_step(q, x["k"], x["v"], x["g"], x["theta"], S[l], o=o_r[l])
+            rd.sw_ska_decode_step(o_r[l], *s_in[l][i], kc[l], vc[l], pos[l], o=o_s[l], workspace=ws[l])
+            q = o_s[l]
+
+    ms = _time(step, steps, warmup)
+    tf = _timing_fields(1e3, "us_per_token")
+    ms_graph = _graph_time(step, pool, max(4, steps // pool))
+    nbytes = layers * (decode_bytes(N, H, d, d) + swska_decode_bytes(N, H, d, d, window))
+    return dict(us_per_token=ms * 1e3, us_per_token_graph=ms_graph * 1e3, tokens_per_s=N / (ms * 1e-3),
+                tokens_per_s_graph=N / (ms_graph * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                gbs_graph=nbytes / (ms_graph * 1e-3) / 1e9, launches_per_token=3 * layers, **tf,
+                config=dict(N=N, H=H, d=d, window=window, layers=layers))
 
 
 def bench_copy(nbytes=1 << 30, steps=5):
@@ -452,6 +565,78 @@ def cpu_baseline(cfg, min_cpu_s=12.0, max_reps=40):
                 nproc=nproc, cpu_model=_cpu_model())
 
 
+def _oracle_cores():
+    return min(os.cpu_count() or 1, 16)
+
+
+def cpu_baseline_long(cfg, T_sample=16384):
+    """The oracle on every head of the long-context prefill over its first
+    T_sample tokens (the per-token cost of the sequential recurrence does not
+    depend on the position), one head per thread."""
+    import oracle
+    import workloads
+    cores = _oracle_cores()
+    x = workloads.scan_inputs(cfg["seed"], cfg["B"], cfg["H"], T_sample, cfg["dk"], cfg["dv"], cfg["dtype"],
+                              gate_mu=cfg["gate_mu"])
+    arrs = [x[n].f64() for n in NAMES]
+    del x
+    c0, t0 = time.process_time(), time.perf_counter()
+    oracle.scan(*arrs, nthreads=cores)
+    dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+    return dict(value=round(cfg["B"] * T_sample / dt, 1), unit="tokens/s", cores=min(cores, cfg["B"] * cfg["H"]),
+                kind="oracle",
+                sample=f"all {cfg['H']} heads over the first {T_sample} of the {cfg['T']} tokens (inputs drawn "
+                       f"with the workload's recipe at that length), fp64 sequential scan, one (b,h) per thread: "
+                       f"{dt:.2f} s wall, {cpu:.1f} s CPU")
+
+
+def cpu_baseline_decode(cfg, steps=6):
+    """The oracle's decode step (single-threaded C loop) over the whole batch of
+    N sequences x H heads, for `steps` steps from zero states."""
+    import oracle
+    import workloads
+    sets = workloads.decode_pool(cfg["seed"], cfg["N"], cfg["H"], cfg["dk"], cfg["dv"], pool=cfg["pool"],
+                                 dtype=cfg["dtype"])
+    S = np.zeros((cfg["N"], cfg["H"], cfg["dk"], cfg["dv"]))
+    xs = [[s[n].f64() for n in NAMES] for s in sets]
+    c0, t0 = time.process_time(), time.perf_counter()
+    for i in range(steps):
+        _, S = oracle.decode(*xs[i % len(xs)], S)
+    dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+    return dict(value=round(steps * cfg["N"] / dt, 1), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{steps} steps of the whole {cfg['N']}-sequence x {cfg['H']}-head batch (fp64 states "
+                       f"{cfg['dk']}x{cfg['dv']}), single-threaded: {dt:.2f} s wall, {cpu:.1f} s CPU; "
+                       f"us per step {dt / steps * 1e6:.0f}")
+
+
+def cpu_baseline_swska(cfg, rows_per_head=128):
+    """The oracle's dense softmax per query row on rows_per_head rows of every
+    head, spread over the part of the sequence where the window is full."""
+    import oracle
+    import workloads
+    cores = _oracle_cores()
+    B, H, T, D, w = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["window"]
+    x = workloads.swska_inputs(cfg["seed"], B, H, T, D, D)
+    ts = np.linspace(w, T - 1, rows_per_head).astype(np.int64)
+    rows = (np.arange(H)[:, None] * T + ts[None, :]).reshape(-1)
+    q, k, v = (x[n].f64() for n in ("q", "k", "v"))
+    del x
+    c0, t0 = time.process_time(), time.perf_counter()
+    oracle.swska(q, k, v, w, rows=rows, nthreads=cores)
+    dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+    # a token is all H heads' rows
+    return dict(value=round(rows.size / H / dt, 1), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{rows_per_head} query rows per head x {H} heads with a full {w}-key window, "
+                       f"fp64 dense softmax per row on {cores} threads: {dt:.2f} s wall, {cpu:.1f} s CPU")
+
+
+def _rl(bound, achieved, peak, unit, traffic, nbytes, **extra):
+    d = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_bytes": nbytes}
+    d.update(extra)
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,8 +644,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode", "backward", "varlen",
-                             "backward_varlen", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode",
+                                                      "backward", "varlen", "backward_varlen", "chain", "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -475,9 +660,9 @@ def main():
 
     if args.only != "all":
         if args.only == "prefill":
-            r = bench_prefill(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup)
+            r = bench_prefill(workloads.CONFIGS["prefill_1p6b_T4096"], args.steps, args.warmup, cold=False)
         elif args.only == "long":
-            r = bench_prefill(workloads.CONFIGS["prefill_long_T131072"], args.steps, args.warmup)
+            r = bench_prefill(workloads.CONFIGS["prefill_long_T131072"], args.steps, args.warmup, cold=False)
         elif args.only == "decode":
             r = bench_decode(workloads.CONFIGS["decode_N256"], args.steps, args.warmup)
         elif args.only == "swska":
@@ -490,39 +675,51 @@ def main():
             r = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
         elif args.only == "backward_varlen":
             r = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
+        elif args.only == "chain":
+            r = bench_mixer_chain(steps=args.steps, warmup=args.warmup)
         else:
             r = bench_copy()
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}),
               flush=True)
         return
 
+    def stage(name):
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+
     cfg = workloads.CONFIGS["prefill_1p6b_T4096"]
-    print("bench: prefill_1p6b_T4096", file=sys.stderr, flush=True)
+    stage("prefill_1p6b_T4096")
     pre = bench_prefill(cfg, args.steps, args.warmup)
-    print("bench: decode_N256", file=sys.stderr, flush=True)
+    stage("decode_N256")
     dec = bench_decode(workloads.CONFIGS["decode_N256"], args.decode_steps, 10)
-    print("bench: prefill_long_T131072", file=sys.stderr, flush=True)
+    stage("prefill_long_T131072")
     lc = workloads.CONFIGS["prefill_long_T131072"]
     lr = bench_prefill(lc, max(3, args.steps // 4), 1)
-    print("bench: swska_T32768_w4096", file=sys.stderr, flush=True)
-    sr = bench_swska(workloads.CONFIGS["swska_T32768_w4096"], max(3, args.steps // 4), 1)
-    print("bench: swska_decode_N64_w4096", file=sys.stderr, flush=True)
+    stage("swska_T32768_w4096")
+    sc = workloads.CONFIGS["swska_T32768_w4096"]
+    sr = bench_swska(sc, max(3, args.steps // 4), 1)
+    stage("swska_decode_N64_w4096")
     sdc = workloads.CONFIGS["swska_decode_N64_w4096"]
     sd = bench_swska_decode(sdc, sdc["steps"], 10)
-    print("bench: backward_1p6b_T4096", file=sys.stderr, flush=True)
+    stage("rodimus_plus_decode_2layer_N16")
+    ch = bench_mixer_chain()
+    stage("backward_1p6b_T4096")
     bw = bench_backward(cfg, max(5, args.steps // 2), 2)
-    print("bench: prefill_varlen_N64_16K", file=sys.stderr, flush=True)
+    stage("prefill_varlen_N64_16K")
     vl = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
-    print("bench: backward_varlen_N64_16K", file=sys.stderr, flush=True)
+    stage("backward_varlen_N64_16K")
     bvl = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], max(5, args.steps // 2), 2)
 
-    cpu = None
+    cpu = cpu_long = cpu_dec = cpu_ska = None
     if not args.no_cpu:
-        print("bench: cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        stage("cpu baselines (fp64 oracle)")
         cpu = cpu_baseline(cfg)
+        cpu_long = cpu_baseline_long(lc)
+        cpu_dec = cpu_baseline_decode(workloads.CONFIGS["decode_N256"])
+        cpu_ska = cpu_baseline_swska(sc)
 
     tr = measured_traffic("prefill_1p6b_T4096", "prefill")
     dtr = measured_traffic("decode_N256", "decode")
+    dtr_pp = measured_traffic("decode_N256_pingpong", "decode")
     line = {
         "metric": METRIC,
         "value": round(pre["tokens_per_s"], 1),
@@ -531,6 +728,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["ms"], 4),
+        "ms_per_step_median": pre["ms_median"],
+        "ms_per_step_min": pre["ms_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -539,66 +738,93 @@ def main():
         "config": {"workload": "prefill_1p6b_T4096", "B": cfg["B"], "T": cfg["T"], "H": cfg["H"],
                    "dk": cfg["dk"], "dv": cfg["dv"], "chunk": cfg["chunk"],
                    "state_dtype": "fp32"},
-        "roofline": {"bound": "hbm", "achieved": round(pre["gbs"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(pre["gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": tr, "kernel": "rodimus_scan_prefill call (segment states + "
-                     "combine + output pass)", "algorithmic_bytes": pre["bytes"],
-                     "mfma_frac": round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "roofline": _rl("hbm", pre["gbs"], HBM_PEAK_GBS, "GB/s", tr, pre["bytes"],
+                        kernel="rodimus_scan_prefill call (segment states + combine + output pass)",
+                        mfma_frac=round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                        cold_cache={"ms_median": round(pre["ms_cold_median"], 4),
+                                    "ms_min": round(pre["ms_cold_min"], 4),
+                                    "achieved": round(pre["gbs_cold"], 1),
+                                    "frac": round(pre["gbs_cold"] / HBM_PEAK_GBS, 4),
+                                    "how": "512 MB written before each call; events around the call only"}),
         "cpu_baseline": cpu,
-        "decode": {"workload": "decode_N256", "us_per_step": round(dec["us_per_step"], 2),
-                   "us_per_step_graph": round(dec["us_per_step_graph"], 2),
-                   "us_per_step_pingpong": round(dec["us_per_step_pingpong"], 2),
-                   "frac_pingpong": round(dec["gbs_pingpong"] / HBM_PEAK_GBS, 4),
-                   "tokens_per_s": round(dec["tokens_per_s"]), "steps": dec["steps"],
-                   "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1),
-                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": dtr,
-                                "kernel": "decode_step_kernel<bf16,128,128>",
-                                "algorithmic_bytes": dec["bytes"]}},
+        "decode": {
+            "workload": "decode_N256", "steps": dec["steps"],
+            "us_per_step": round(dec["us_per_step_pingpong"], 2),
+            "tokens_per_s": round(dec["tokens_per_s_pingpong"]),
+            **dec["timing_pingpong"],
+            "roofline": _rl("hbm", dec["gbs_pingpong"], HBM_PEAK_GBS, "GB/s", dtr_pp, dec["bytes"],
+                            kernel="decode_step_kernel<bf16,128,128>",
+                            working_set="S_in and S_out alternate between two 268 MB buffers (537 MB, "
+                                        "twice the 256 MB Infinity Cache): HBM-true"),
+            "in_place_cache_assisted": {
+                "us_per_step": round(dec["us_per_step"], 2), **dec["timing"],
+                "us_per_step_graph": round(dec["us_per_step_graph"], 2),
+                "tokens_per_s": round(dec["tokens_per_s"]),
+                "achieved": round(dec["gbs"], 1), "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": dtr,
+                "note": "state updated in place; the 268 MB state is about the 256 MB Infinity Cache's size, "
+                        "so part of each step is served from that cache"},
+            f"in_place_N{dec['big_n']}": {
+                "us_per_step": round(dec["us_per_step_big"], 2), **dec["timing_big"],
+                "achieved": round(dec["gbs_big"], 1), "frac": round(dec["gbs_big"] / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": dec["bytes_big"],
+                "note": f"{dec['big_n']} sequences: a {dec['big_n'] * 16 * 65536 / 1e9:.2f} GB state updated in "
+                        "place, far larger than the cache: HBM-true"},
+            "cpu_baseline": cpu_dec},
         "extras": {
             "prefill_long_T131072": {
-                "ms": round(lr["ms"], 4), "tokens_per_s": round(lr["tokens_per_s"]),
-                "roofline": {"bound": "hbm", "achieved": round(lr["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(lr["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("prefill_long_T131072", "prefill"),
-                             "algorithmic_bytes": lr["bytes"]}},
+                "ms": round(lr["ms"], 4), "ms_median": lr["ms_median"], "ms_min": lr["ms_min"],
+                "tokens_per_s": round(lr["tokens_per_s"]),
+                "roofline": _rl("hbm", lr["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("prefill_long_T131072", "prefill"), lr["bytes"],
+                                cold_cache={"ms_median": round(lr["ms_cold_median"], 4),
+                                            "frac": round(lr["gbs_cold"] / HBM_PEAK_GBS, 4)}),
+                "cpu_baseline": cpu_long},
             "swska_T32768_w4096": {
-                "ms": round(sr["ms"], 4), "tokens_per_s": round(sr["tokens_per_s"]),
-                "roofline": {"bound": "mfma", "achieved": round(sr["tflops"], 1),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(sr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": measured_traffic("swska_T32768_w4096", "swska"),
-                             "algorithmic_bytes": sr["bytes"]}},
+                "ms": round(sr["ms"], 4), "ms_median": sr["ms_median"], "ms_min": sr["ms_min"],
+                "tokens_per_s": round(sr["tokens_per_s"]),
+                "roofline": _rl("mfma", sr["tflops"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                measured_traffic("swska_T32768_w4096", "swska"), sr["bytes"]),
+                "cpu_baseline": cpu_ska},
             "swska_decode_N64_w4096": {
-                "us_per_step": round(sd["us_per_step"], 2), "tokens_per_s": round(sd["tokens_per_s"]),
+                "us_per_step": round(sd["us_per_step"], 2), "us_per_step_median": sd["us_per_step_median"],
+                "us_per_step_min": sd["us_per_step_min"], "tokens_per_s": round(sd["tokens_per_s"]),
                 "us_per_step_graph": round(sd["us_per_step_graph"], 2),
                 "steps": sd["steps"],
-                "roofline": {"bound": "hbm", "achieved": round(sd["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(sd["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("swska_decode_N64_w4096", "swska_decode"),
-                             "algorithmic_bytes": sd["bytes"]}},
+                "roofline": _rl("hbm", sd["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("swska_decode_N64_w4096", "swska_decode"), sd["bytes"],
+                                working_set="1.14 GB of window caches per step: HBM-true"),
+                "cpu_baseline": None if cpu_ska is None else dict(
+                    cpu_ska, sample="the SW-SKA rows above: a decode token of one sequence is one full-window "
+                                    "row per head, the same oracle work")},
+            "rodimus_plus_decode_2layer_N16": {
+                "us_per_token": round(ch["us_per_token"], 2), "us_per_token_median": ch["us_per_token_median"],
+                "us_per_token_min": ch["us_per_token_min"],
+                "us_per_token_graph": round(ch["us_per_token_graph"], 2),
+                "tokens_per_s": round(ch["tokens_per_s"]), "tokens_per_s_graph": round(ch["tokens_per_s_graph"]),
+                "launches_per_token": ch["launches_per_token"], "config": ch["config"],
+                "roofline": _rl("hbm", ch["gbs"], HBM_PEAK_GBS, "GB/s", None, ch["bytes"],
+                                graph_frac=round(ch["gbs_graph"] / HBM_PEAK_GBS, 4))},
             "backward_1p6b_T4096": {
-                "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"]),
-                "roofline": {"bound": "hbm", "achieved": round(bw["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(bw["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("backward_1p6b_T4096", "backward"),
-                             "kernel": "rodimus_scan_backward call (state passes + combine + "
-                             "gradients + fallback)", "algorithmic_bytes": bw["bytes"],
-                             "workspace_bytes": bw["workspace_bytes"]}},
+                "ms": round(bw["ms"], 4), "ms_median": bw["ms_median"], "ms_min": bw["ms_min"],
+                "tokens_per_s": round(bw["tokens_per_s"]),
+                "roofline": _rl("hbm", bw["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("backward_1p6b_T4096", "backward"), bw["bytes"],
+                                kernel="rodimus_scan_backward call (state passes + combine + gradients + fallback)",
+                                workspace_bytes=bw["workspace_bytes"])},
             "prefill_varlen_N64_16K": {
-                "ms": round(vl["ms"], 4), "tokens_per_s": round(vl["tokens_per_s"]),
+                "ms": round(vl["ms"], 4), "ms_median": vl["ms_median"], "ms_min": vl["ms_min"],
+                "tokens_per_s": round(vl["tokens_per_s"]),
                 "sequences": vl["sequences"], "min_len": vl["min_len"], "max_len": vl["max_len"],
-                "roofline": {"bound": "hbm", "achieved": round(vl["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(vl["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("prefill_varlen_N64_16K", "prefill"),
-                             "algorithmic_bytes": vl["bytes"]}},
+                "roofline": _rl("hbm", vl["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("prefill_varlen_N64_16K", "prefill"), vl["bytes"])},
             "backward_varlen_N64_16K": {
-                "ms": round(bvl["ms"], 4), "tokens_per_s": round(bvl["tokens_per_s"]),
+                "ms": round(bvl["ms"], 4), "ms_median": bvl["ms_median"], "ms_min": bvl["ms_min"],
+                "tokens_per_s": round(bvl["tokens_per_s"]),
                 "sequences": bvl["sequences"], "min_len": bvl["min_len"], "max_len": bvl["max_len"],
-                "roofline": {"bound": "hbm", "achieved": round(bvl["gbs"], 1), "peak": HBM_PEAK_GBS,
-                             "unit": "GB/s", "frac": round(bvl["gbs"] / HBM_PEAK_GBS, 4),
-                             "traffic": measured_traffic("backward_varlen_N64_16K", "backward"),
-                             "algorithmic_bytes": bvl["bytes"], "workspace_bytes": bvl["workspace_bytes"]}},
+                "roofline": _rl("hbm", bvl["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("backward_varlen_N64_16K", "backward"), bvl["bytes"],
+                                workspace_bytes=bvl["workspace_bytes"])},
         },
     }
     print(json.dumps(line), flush=True)
