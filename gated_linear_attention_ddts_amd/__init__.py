@@ -8,6 +8,9 @@ Entry points (same names as the C ABI):
 
 * :func:`rodimus_scan_prefill` -- chunkwise-parallel prefill of the DDTS-gated
   recurrence; returns ``(o, S_T)``.
+* :func:`rodimus_scan_prefill_noalloc` -- the same prefill into caller-given
+  outputs, with its scratch in the library's fixed device array: allocates
+  nothing, here or in the library.
 * :func:`rodimus_scan_backward` -- gradients of the prefill with respect to q, k,
   v, g, tau and S0 (fp32); returns a dict.
 * :func:`rodimus_decode_step`  -- one recurrent step on a resident state
@@ -34,9 +37,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librodimus.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
-EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill",
+EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill", "rodimus_scan_prefill_noalloc",
             "rodimus_scan_prefill_varlen_workspace_bytes", "rodimus_scan_prefill_varlen",
             "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward",
             "rodimus_scan_backward_varlen_workspace_bytes", "rodimus_scan_backward_varlen", "rodimus_decode_step",
@@ -65,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_scan_prefill_workspace_bytes.restype = sz
         L.rodimus_scan_prefill.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
         L.rodimus_scan_prefill.restype = i
+        L.rodimus_scan_prefill_noalloc.argtypes = [vp] * 8 + [i] * 7 + [vp]
+        L.rodimus_scan_prefill_noalloc.restype = i
         L.rodimus_scan_prefill_varlen_workspace_bytes.argtypes = [i] * 7
         L.rodimus_scan_prefill_varlen_workspace_bytes.restype = sz
         L.rodimus_scan_prefill_varlen.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
@@ -176,6 +181,33 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
                                     _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "rodimus_scan_prefill")
     return o, S_T
+
+
+def rodimus_scan_prefill_noalloc(q, k, v, g, tau, S0=None, chunk: int = 64, *, o, S_T=None,
+                                 stream=None) -> None:
+    """rodimus_scan_prefill into the caller's o [B,H,T,dv] (and S_T
+    [B,H,dk,dv] float32, or None to skip it), without any allocation: the
+    segment states live in the library's fixed per-GPU scratch array.  Calls
+    that may overlap on one GPU must be serialised by the caller."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for x in (k, g, tau, v):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, g, tau must share one dtype")
+    for x, nm in ((k, "k"), (g, "g"), (tau, "tau")):
+        _shape(x, (B, H, T, dk), nm)
+    _shape(v, (B, H, T, dv), "v")
+    _shape(S0, (B, H, dk, dv), "S0")
+    _shape(o, (B, H, T, dv), "o")
+    _shape(S_T, (B, H, dk, dv), "S_T")
+    for x, nm in ((S0, "S0"), (S_T, "S_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    _out_dtype(o, q.dtype, "o")
+    st = lib().rodimus_scan_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(tau), _ptr(S0),
+                                            _ptr(o), _ptr(S_T), B, H, T, dk, dv, chunk, dt, _stream(stream))
+    _check(st, "rodimus_scan_prefill_noalloc")
 
 
 def rodimus_scan_prefill_varlen_workspace_bytes(N, H, max_seqlen, dk, dv, chunk=64, dtype=BF16) -> int:

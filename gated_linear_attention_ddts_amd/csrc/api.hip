@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/rodimus.h"
 #include "launch.h"
 
@@ -44,6 +46,8 @@ const char *rodimus_status_string(int status) {
         case RODIMUS_ERR_INVALID_ARG: return "RODIMUS_ERR_INVALID_ARG: invalid argument";
         case RODIMUS_ERR_UNSUPPORTED: return "RODIMUS_ERR_UNSUPPORTED: shape/dtype not compiled";
         case RODIMUS_ERR_HIP: return "RODIMUS_ERR_HIP: HIP runtime error";
+        case RODIMUS_ERR_TOO_LARGE:
+            return "RODIMUS_ERR_TOO_LARGE: needs more scratch than the fixed no-allocation buffer holds";
         default: return "RODIMUS_UNKNOWN_STATUS";
     }
 }
@@ -76,10 +80,46 @@ size_t rodimus_scan_prefill_workspace_bytes(int B, int H, int T, int dk, int dv,
     return plan_scan(B, H, T, dk, dv, chunk == 0 ? 64 : chunk, dtype).workspace_bytes;
 }
 
-int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void *g,
-                         const void *tau, const float *S0, void *o, float *S_T,
-                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
-                         void *workspace, size_t workspace_bytes, void *stream) {
+// ------------------------------------------------------------ fixed scratch
+// rodimus_scan_prefill_noalloc keeps the segment-parallel states in this
+// array instead of a caller workspace.  34 MiB holds the largest segment plan
+// of any prefill (33,684,480 bytes: B*H = 1, 256 segments of 2 sub-segments).
+// Each device holds its own copy, from the first call on it until the process
+// ends.  In host code the array's name is only a host-side stand-in: the
+// kernels get its device address from scratch_on_current_device().
+constexpr size_t kScratchBytes = (size_t)34 << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current, then kept.
+static int scratch_on_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return RODIMUS_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return RODIMUS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return RODIMUS_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RODIMUS_OK;
+}
+
+// The prefill behind both entry points.  With use_scratch, the segment states
+// go to this device's fixed scratch array (looked up only once validation has
+// passed and only if the plan needs it) instead of the caller's workspace.
+static int scan_prefill_impl(const void *q, const void *k, const void *v, const void *g,
+                             const void *tau, const float *S0, void *o, float *S_T,
+                             int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                             void *workspace, size_t workspace_bytes, bool use_scratch, void *stream) {
     if (!scan_sizes_ok(B, H, T, dk, dv, chunk, dtype)) return RODIMUS_ERR_INVALID_ARG;
     if (!ok_opt_ptr(S0) || !ok_opt_ptr(S_T) || !ok_opt_ptr(workspace))
         return RODIMUS_ERR_INVALID_ARG;
@@ -99,6 +139,12 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
         return RODIMUS_ERR_INVALID_ARG;
     ScanPlan plan = plan_scan(B, H, T, dk, dv, chunk, dtype);
     if (!scan_launch_fits(plan, B, H, T, chunk)) return RODIMUS_ERR_INVALID_ARG;
+    if (use_scratch && plan.workspace_bytes > 0) {
+        if (plan.workspace_bytes > kScratchBytes) return RODIMUS_ERR_TOO_LARGE;
+        const int rc = scratch_on_current_device(&workspace);
+        if (rc != RODIMUS_OK) return rc;
+        workspace_bytes = kScratchBytes;
+    }
     if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
         return RODIMUS_ERR_INVALID_ARG;
     ScanArgs a{q, k, v, g, tau, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, workspace,
@@ -106,6 +152,22 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
     if (plan.mfma) launch_scan_mfma(a, plan, st);
     else launch_scan_generic(a, st);
     return hip_status();
+}
+
+int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void *g,
+                         const void *tau, const float *S0, void *o, float *S_T,
+                         int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    return scan_prefill_impl(q, k, v, g, tau, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, workspace,
+                             workspace_bytes, false, stream);
+}
+
+int rodimus_scan_prefill_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                 const void *tau, const float *S0, void *o, float *S_T,
+                                 int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                 void *stream) {
+    return scan_prefill_impl(q, k, v, g, tau, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, nullptr, 0,
+                             true, stream);
 }
 
 size_t rodimus_scan_prefill_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,

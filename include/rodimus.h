@@ -39,8 +39,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All pointers are DEVICE pointers (hipMalloc'd or equivalent) owned by the
- *    caller; the library keeps no pointer after the call returns, allocates
- *    nothing and has no mutable global state (thread-safe).
+ *    caller; the library keeps no pointer after the call returns and
+ *    allocates nothing.  Its only global state is the fixed scratch array of
+ *    rodimus_scan_prefill_noalloc and that array's address per device; every
+ *    other entry point is thread-safe.
  *  - Tensors are contiguous, row-major, 16-byte aligned.
  *  - dtype selects the element type of q, k, v, g, tau and o:
  *    RODIMUS_F32 (float) or RODIMUS_BF16 (bfloat16 bit patterns).  Recurrent
@@ -75,7 +77,8 @@ typedef enum {
     RODIMUS_OK = 0,
     RODIMUS_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, small workspace */
     RODIMUS_ERR_UNSUPPORTED = -2, /* valid but outside the compiled kernel set */
-    RODIMUS_ERR_HIP = -3          /* the HIP runtime reported an error */
+    RODIMUS_ERR_HIP = -3,         /* the HIP runtime reported an error */
+    RODIMUS_ERR_TOO_LARGE = -4    /* needs more scratch than rodimus_scan_prefill_noalloc's fixed buffer */
 } rodimus_status;
 
 typedef enum { RODIMUS_F32 = 0, RODIMUS_BF16 = 1 } rodimus_dtype;
@@ -122,6 +125,31 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
                          const void *tau, const float *S0, void *o, float *S_T,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rodimus_scan_prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results (bit for bit)
+ * and kernels as rodimus_scan_prefill, except that the segment-parallel
+ * states live in a fixed array inside the library instead of a caller
+ * workspace: 34 MiB of device memory per GPU, held from the first call on that
+ * GPU until the process ends.  It is large enough for every prefill the
+ * library accepts (the largest segment plan needs 33,684,480 bytes);
+ * a plan beyond it would return RODIMUS_ERR_TOO_LARGE.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * its first call on a GPU looks up the array's device address there
+ * (hipGetSymbolAddress, current device).  The caller passes inputs and
+ * outputs as for rodimus_scan_prefill.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels write every element they read, so nothing needs
+ * clearing): calls that may overlap on one GPU -- on different streams, or
+ * from several host threads -- race and must be serialised by the caller.
+ */
+int rodimus_scan_prefill_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                 const void *tau, const float *S0, void *o, float *S_T,
+                                 int B, int H, int T, int dk, int dv, int chunk, int dtype,
+                                 void *stream);
 
 /*
  * rodimus_scan_prefill over a packed batch of sequences of different lengths

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (rd.OK, rd.ERR_INVALID_ARG, rd.ERR_UNSUPPORTED, rd.ERR_HIP):
+    for code in (rd.OK, rd.ERR_INVALID_ARG, rd.ERR_UNSUPPORTED, rd.ERR_HIP, rd.ERR_TOO_LARGE):
         s = rd.status_string(code)
         assert s.startswith("RODIMUS_")
     assert rd.status_string(12345) == "RODIMUS_UNKNOWN_STATUS"
@@ -335,3 +335,37 @@ def test_swska_rejects_a_grid_beyond_hip_limits():
     assert ska(B=1, H=1 << 10, T=1 << 21) == rd.ERR_INVALID_ARG
     # d = 64: 256 threads per 128 query rows
     assert ska(B=1, H=1 << 10, T=1 << 21, dk=64, dv=64) == rd.ERR_INVALID_ARG
+
+
+# ------------------------------------------------- prefill without allocation
+def scan_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, tau=FAKE, S0=None, o=FAKE, S_T=None, B=1, H=1, T=8,
+             dk=16, dv=16, chunk=64, dtype=rd.BF16, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_prefill_noalloc(a["q"], a["k"], a["v"], a["g"], a["tau"], a["S0"], a["o"],
+                                                 a["S_T"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                                                 a["chunk"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(tau=None), dict(o=None), dict(q=MISALIGNED), dict(S0=MISALIGNED), dict(S_T=MISALIGNED),
+    dict(B=-1), dict(T=-1), dict(dk=8), dict(dv=136), dict(chunk=8), dict(dtype=2), dict(S0=FAKE, S_T=FAKE),
+    dict(B=1 << 13, H=1 << 10, T=64, dk=128, dv=128),      # grid beyond HIP's limit
+])
+def test_scan_noalloc_rejects_before_any_hip_call(kw):
+    # the scratch array's address is looked up only after validation has passed
+    assert scan_noalloc(**kw) == rd.ERR_INVALID_ARG
+
+
+def test_scan_noalloc_empty_is_noop():
+    assert scan_noalloc(B=0, q=None) == rd.OK
+    assert scan_noalloc(T=0, q=None, o=None) == rd.OK
+
+
+def test_scan_noalloc_scratch_covers_every_segment_plan():
+    # the fixed array (34 MiB) holds the workspace of the largest segment plan
+    # the prefill can make, so the no-allocation call never runs out of scratch
+    worst = max(rd.rodimus_scan_prefill_workspace_bytes(1, bh, T, 128, 128, c, rd.BF16)
+                for bh in (1, 2, 3, 5, 16, 17, 64, 100, 128, 255) for T in (4096, 32704, 131072, 8388607)
+                for c in (32, 64))
+    assert worst == 33684480 <= 34 << 20
