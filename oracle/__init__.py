@@ -13,7 +13,10 @@ computes, and the passages it follows, are stated in the C file's header:
   o_t = q_t S_t, token by token,
 * :func:`decode` -- one step of the same recurrence on a persistent state,
 * :func:`swska`  -- sliding-window attention with one key matrix shared by all
-  heads, dense softmax per query row.
+  heads, dense softmax per query row,
+* :func:`lowrank_gate_logits` / :func:`scan_lowrank` -- gate logits from
+  rank-R factor rows shared by the heads (our reading of the gates' learnable
+  weights), and the recurrence on them.
 """
 from __future__ import annotations
 
@@ -58,6 +61,8 @@ def _load():
                                      [ctypes.POINTER(ctypes.c_longlong), ctypes.c_longlong,
                                       ctypes.c_int])
         lib.oracle_swska.restype = ctypes.c_int
+        lib.oracle_lowrank_gate_logits.argtypes = [ctypes.c_int] * 5 + [dp] * 8
+        lib.oracle_lowrank_gate_logits.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -101,6 +106,31 @@ def scan(q, k, v, g, theta, S0=None, nthreads: int = 1):
                              _ptr(S0), _ptr(o), _ptr(ST), int(nthreads))
     assert rc == 0
     return o, ST
+
+
+def lowrank_gate_logits(zg, zt, Ug, bg, Ut, bt, H=None):
+    """Gate logits from rank-R factor rows shared by the heads (our reading of
+    the gates' learnable weights; see the C file):  g = silu(zg) Ug^T + bg,
+    theta = zt Ut^T + bt per head.  zg, zt: [B,T,R]; Ug, Ut: [H,dk,R];
+    bg, bt: [H,dk].  Returns (g, theta) [B,H,T,dk] in fp64."""
+    zg, zt, Ug, bg, Ut, bt = (_f64(x) for x in (zg, zt, Ug, bg, Ut, bt))
+    B, T, R = zg.shape
+    H, dk, R2 = Ug.shape
+    assert R2 == R and zt.shape == zg.shape and Ut.shape == Ug.shape
+    assert bg.shape == (H, dk) and bt.shape == (H, dk)
+    g = np.empty((B, H, T, dk))
+    th = np.empty((B, H, T, dk))
+    rc = _load().oracle_lowrank_gate_logits(B, H, T, dk, R, _ptr(zg), _ptr(zt), _ptr(Ug), _ptr(bg), _ptr(Ut),
+                                            _ptr(bt), _ptr(g), _ptr(th))
+    assert rc == 0
+    return g, th
+
+
+def scan_lowrank(q, k, v, zg, zt, Ug, bg, Ut, bt, S0=None, nthreads: int = 1):
+    """The recurrence with gate logits from rank-R factors: lowrank_gate_logits
+    followed by scan.  Returns (o, S_T) in fp64."""
+    g, th = lowrank_gate_logits(zg, zt, Ug, bg, Ut, bt)
+    return scan(q, k, v, g, th, S0=S0, nthreads=nthreads)
 
 
 def scan_backward(q, k, v, g, theta, dO, S0=None, dST=None, nthreads: int = 1):

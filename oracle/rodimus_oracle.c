@@ -66,6 +66,50 @@ void oracle_gates(const double *g, const double *theta, size_t n,
     }
 }
 
+/* ---------------------------------------------------- low-rank gate logits */
+
+/* silu(x) = x * sigmoid(x) */
+static double silu(double x) { return x * sigmoid(x); }
+
+/* The gate logits from rank-R factors (our reading: the Rodimus block
+ * paragraph of the CodeFuse article computes the selection and temperature
+ * gates from the token through learnable weights, and section 3 of the
+ * Rodimus* deployment blog names SiLU as the selection gate's activation; the
+ * projection itself is not printed).  Each token's hidden state has been
+ * projected to two factor rows z_g, z_tau in R^R shared by all heads; per head
+ * h and key channel c:
+ *     g[b,h,t,c]     = sum_r silu(z_g[b,t,r]) U_g[h,c,r]   + b_g[h,c]
+ *     theta[b,h,t,c] = sum_r      z_tau[b,t,r] U_tau[h,c,r] + b_tau[h,c]
+ * Layouts: zg, zt [B,T,R]; Ug, Ut [H,dk,R]; bg, bt [H,dk]; g, theta
+ * [B,H,T,dk]. */
+int oracle_lowrank_gate_logits(int B, int H, int T, int dk, int R,
+                               const double *zg, const double *zt,
+                               const double *Ug, const double *bg,
+                               const double *Ut, const double *bt,
+                               double *g, double *theta) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || R <= 0) return -1;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int t = 0; t < T; ++t) {
+                const double *zgt = zg + ((size_t)b * T + t) * R;
+                const double *ztt = zt + ((size_t)b * T + t) * R;
+                double *gt = g + (((size_t)b * H + h) * T + t) * dk;
+                double *tht = theta + (((size_t)b * H + h) * T + t) * dk;
+                for (int c = 0; c < dk; ++c) {
+                    const double *ug = Ug + ((size_t)h * dk + c) * R;
+                    const double *ut = Ut + ((size_t)h * dk + c) * R;
+                    double sg = bg[(size_t)h * dk + c], st = bt[(size_t)h * dk + c];
+                    for (int r = 0; r < R; ++r) {
+                        sg += silu(zgt[r]) * ug[r];
+                        st += ztt[r] * ut[r];
+                    }
+                    gt[c] = sg;
+                    tht[c] = st;
+                }
+            }
+    return 0;
+}
+
 /* --------------------------------------------------------------- the scan */
 
 typedef struct {

@@ -20,6 +20,15 @@ extern "C" {
 void oracle_gates(const double *g, const double *theta, size_t n,
                   double *log_a, double *log_beta);
 
+/* Gate logits from rank-R factors shared by the heads:
+ *   g = silu(zg) Ug^T + bg,  theta = zt Ut^T + bt   (per head h, channel c)
+ * zg, zt [B,T,R]; Ug, Ut [H,dk,R]; bg, bt [H,dk]; g, theta [B,H,T,dk]. */
+int oracle_lowrank_gate_logits(int B, int H, int T, int dk, int R,
+                               const double *zg, const double *zt,
+                               const double *Ug, const double *bg,
+                               const double *Ut, const double *bt,
+                               double *g, double *theta);
+
 /* Sequential recurrence over T tokens for every (b,h); nthreads splits (b,h). */
 int oracle_scan(int B, int H, int T, int dk, int dv,
                 const double *q, const double *k, const double *v,

@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_backward_pins as bpins
+from tests import test_oracle_lowrank_pins as lpins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "rodimus_oracle.c")
@@ -38,6 +39,11 @@ PIN_TESTS = [
     lambda: pins.test_swska_constant_key_is_window_mean(),
     lambda: bpins.test_backward_matches_central_differences(True),
     lambda: bpins.test_backward_reduces_to_linear_attention_gradients(),
+    lambda: lpins.test_lowrank_logits_match_numpy_contraction(1, (2, 3, 7, 5, 4)),
+    lambda: lpins.test_lowrank_silu_values_from_the_tanh_identity(),
+    lambda: lpins.test_lowrank_bias_only(),
+    lambda: lpins.test_lowrank_symmetries(),
+    lambda: lpins.test_lowrank_scan_geometric_closed_form(0.7, 0.3),
 ]
 
 MUTATIONS = {
@@ -71,6 +77,16 @@ MUTATIONS = {
     "bwd_dq_previous_state": ("for (int j = 0; j < dv; ++j) acc += dOt[j] * St[i * dv + j];",
                               "for (int j = 0; j < dv; ++j) acc += dOt[j] * Sp[i * dv + j];"),
     "bwd_dk_missing_beta": ("dkt[i] = bt[i] * d_bk;", "dkt[i] = d_bk;"),
+    "lowrank_silu_as_sigmoid": ("static double silu(double x) { return x * sigmoid(x); }",
+                                "static double silu(double x) { return sigmoid(x); }"),
+    "lowrank_factor_transposed": ("sg += silu(zgt[r]) * ug[r];",
+                                  "sg += silu(zgt[r]) * Ug[((size_t)h * R + r) * dk + c];"),
+    "lowrank_bias_dropped": ("double sg = bg[(size_t)h * dk + c], st = bt[(size_t)h * dk + c];",
+                             "double sg = 0.0, st = bt[(size_t)h * dk + c];"),
+    "lowrank_temperature_activated": ("st += ztt[r] * ut[r];", "st += silu(ztt[r]) * ut[r];"),
+    "lowrank_factor_rows_swapped": ("sg += silu(zgt[r]) * ug[r];", "sg += silu(ztt[r]) * ug[r];"),
+    "lowrank_head_ignored": ("const double *ug = Ug + ((size_t)h * dk + c) * R;",
+                             "const double *ug = Ug + ((size_t)0 * dk + c) * R;"),
 }
 
 
@@ -92,7 +108,8 @@ def _build_variant(tmp_path, old=None, new=None):
 def _use(path):
     real = oracle._load()
     lib = ctypes.CDLL(path)
-    for name in ("oracle_gates", "oracle_scan", "oracle_decode", "oracle_swska", "oracle_scan_backward"):
+    for name in ("oracle_gates", "oracle_scan", "oracle_decode", "oracle_swska", "oracle_scan_backward",
+                 "oracle_lowrank_gate_logits"):
         getattr(lib, name).argtypes = getattr(real, name).argtypes
         getattr(lib, name).restype = getattr(real, name).restype
     oracle._lib = lib
