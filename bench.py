@@ -209,6 +209,42 @@ def bench_prefill(cfg, steps, warmup, cold=True):
     return r
 
 
+def lowrank_bytes(B, H, T, dk, dv, R):
+    # q, k, v in and o out (bf16) per token-head; the factor rows per token
+    # (shared by the heads); the per-head factors and biases; the fp32 S_T
+    return (B * H * T * (2 * dk + dv + dv) * 2 + B * T * 2 * R * 2 + H * (2 * dk * R * 2 + 2 * dk * 4)
+            + B * H * dk * dv * 4)
+
+
+def bench_lowrank(cfg, steps, warmup, bias_sigma=None):
+    """The 1.6B-shaped prefill with the gate logits expanded in-kernel from
+    rank-R factor rows (g and tau never stored).  bias_sigma overrides the
+    workload's bias spread (random biases give some channels a decay fast
+    enough to send a few chunks to the token-by-token fallback)."""
+    import torch
+    import gated_linear_attention_ddts_amd as rd
+    import workloads
+    B, H, T, dk, dv, C, R = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"], cfg["chunk"], cfg["R"]
+    bs = cfg["bias_sigma"] if bias_sigma is None else bias_sigma
+    x = workloads.lowrank_inputs(cfg["seed"], B, H, T, dk, dv, R, bias_sigma=bs)
+    names = ("q", "k", "v", "zg", "zt", "Ug", "bg", "Ut", "bt")
+    d = {n: _dev(x[n]) for n in names}
+    del x
+    o = torch.empty(B, H, T, dv, dtype=torch.bfloat16, device="cuda")
+    ST = torch.empty(B, H, dk, dv, dtype=torch.float32, device="cuda")
+    nws = rd.rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, C, rd.BF16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rd.rodimus_scan_prefill_lowrank(*(d[n] for n in names), None, C, o=o, S_T=ST, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    tf = _timing_fields()
+    nbytes = lowrank_bytes(B, H, T, dk, dv, R)
+    return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                bytes_per_token_head=nbytes / (B * H * T), **tf)
+
+
 def bench_varlen(cfg, steps, warmup):
     import torch
     import gated_linear_attention_ddts_amd as rd
@@ -645,7 +681,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "long", "swska", "swska_decode",
-                                                      "backward", "varlen", "backward_varlen", "chain", "copy"])
+                                                      "backward", "varlen", "backward_varlen", "lowrank", "chain",
+                                                      "copy"])
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not run here. Every (b,h) pair, "
@@ -675,6 +712,8 @@ def main():
             r = bench_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
         elif args.only == "backward_varlen":
             r = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], args.steps, args.warmup)
+        elif args.only == "lowrank":
+            r = bench_lowrank(workloads.CONFIGS["prefill_lowrank_1p6b_T4096"], args.steps, args.warmup)
         elif args.only == "chain":
             r = bench_mixer_chain(steps=args.steps, warmup=args.warmup)
         else:
@@ -702,6 +741,10 @@ def main():
     sd = bench_swska_decode(sdc, sdc["steps"], 10)
     stage("rodimus_plus_decode_2layer_N16")
     ch = bench_mixer_chain()
+    stage("prefill_lowrank_1p6b_T4096")
+    lrc = workloads.CONFIGS["prefill_lowrank_1p6b_T4096"]
+    lrk = bench_lowrank(lrc, args.steps, args.warmup)
+    lrk_rb = bench_lowrank(lrc, args.steps, args.warmup, bias_sigma=0.5)
     stage("backward_1p6b_T4096")
     bw = bench_backward(cfg, max(5, args.steps // 2), 2)
     stage("prefill_varlen_N64_16K")
@@ -805,6 +848,16 @@ def main():
                 "launches_per_token": ch["launches_per_token"], "config": ch["config"],
                 "roofline": _rl("hbm", ch["gbs"], HBM_PEAK_GBS, "GB/s", None, ch["bytes"],
                                 graph_frac=round(ch["gbs_graph"] / HBM_PEAK_GBS, 4))},
+            "prefill_lowrank_1p6b_T4096": {
+                "ms": round(lrk["ms"], 4), "ms_median": lrk["ms_median"], "ms_min": lrk["ms_min"],
+                "tokens_per_s": round(lrk["tokens_per_s"]),
+                "bytes_per_token_head": round(lrk["bytes_per_token_head"], 1),
+                "vs_logit_input_prefill": round(pre["ms"] / lrk["ms"], 3),
+                "ms_random_biases": round(lrk_rb["ms"], 4),
+                "roofline": _rl("hbm", lrk["gbs"], HBM_PEAK_GBS, "GB/s",
+                                measured_traffic("prefill_lowrank_1p6b_T4096", "prefill"), lrk["bytes"],
+                                kernel="rodimus_scan_prefill_lowrank call (segment states + combine + "
+                                       "output pass, gate logits from rank-16 factors in-kernel)")},
             "backward_1p6b_T4096": {
                 "ms": round(bw["ms"], 4), "ms_median": bw["ms_median"], "ms_min": bw["ms_min"],
                 "tokens_per_s": round(bw["tokens_per_s"]),

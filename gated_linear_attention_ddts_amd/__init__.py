@@ -8,6 +8,8 @@ Entry points (same names as the C ABI):
 
 * :func:`rodimus_scan_prefill` -- chunkwise-parallel prefill of the DDTS-gated
   recurrence; returns ``(o, S_T)``.
+* :func:`rodimus_scan_prefill_lowrank` -- the prefill with the gate logits
+  expanded inside the kernels from rank-16 factor rows; returns ``(o, S_T)``.
 * :func:`rodimus_scan_prefill_noalloc` -- the same prefill into caller-given
   outputs, with its scratch in the library's fixed device array: allocates
   nothing, here or in the library.
@@ -40,6 +42,7 @@ LIB_PATH = os.path.join(_HERE, "librodimus.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 EXPORTED = ("rodimus_scan_prefill_workspace_bytes", "rodimus_scan_prefill", "rodimus_scan_prefill_noalloc",
+            "rodimus_scan_prefill_lowrank",
             "rodimus_scan_prefill_varlen_workspace_bytes", "rodimus_scan_prefill_varlen",
             "rodimus_scan_backward_workspace_bytes", "rodimus_scan_backward",
             "rodimus_scan_backward_varlen_workspace_bytes", "rodimus_scan_backward_varlen", "rodimus_decode_step",
@@ -70,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.rodimus_scan_prefill.restype = i
         L.rodimus_scan_prefill_noalloc.argtypes = [vp] * 8 + [i] * 7 + [vp]
         L.rodimus_scan_prefill_noalloc.restype = i
+        L.rodimus_scan_prefill_lowrank.argtypes = [vp] * 12 + [i] * 8 + [vp, sz, vp]
+        L.rodimus_scan_prefill_lowrank.restype = i
         L.rodimus_scan_prefill_varlen_workspace_bytes.argtypes = [i] * 7
         L.rodimus_scan_prefill_varlen_workspace_bytes.restype = sz
         L.rodimus_scan_prefill_varlen.argtypes = [vp] * 9 + [i] * 8 + [vp, sz, vp]
@@ -180,6 +185,50 @@ def rodimus_scan_prefill(q, k, v, g, tau, S0=None, chunk: int = 64, *, o=None, S
                                     _ptr(o), _ptr(S_T), B, H, T, dk, dv, chunk, dt,
                                     _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "rodimus_scan_prefill")
+    return o, S_T
+
+
+def rodimus_scan_prefill_lowrank(q, k, v, zg, zt, Ug, bg, Ut, bt, S0=None, chunk: int = 64, *, o=None,
+                                 S_T=None, want_state: bool = True, workspace=None,
+                                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """q, k: [B,H,T,dk]; v: [B,H,T,dv] (bf16); zg, zt: [B,T,R] bf16 factor rows
+    shared by the heads; Ug, Ut: [H,dk,R] bf16; bg, bt: [H,dk] float32.
+    Per head: g = silu(zg) Ug^T + bg, tau = zt Ut^T + bt, then the prefill.
+    Returns (o [B,H,T,dv], S_T [B,H,dk,dv] float32 or None)."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    R = zg.shape[-1]
+    dt = _dtype_code(q)
+    for x in (k, v, zg, zt, Ug, Ut):
+        if x.dtype != q.dtype:
+            raise TypeError("q, k, v, zg, zt, Ug, Ut must share one dtype")
+    _shape(k, (B, H, T, dk), "k")
+    _shape(v, (B, H, T, dv), "v")
+    _shape(zg, (B, T, R), "zg")
+    _shape(zt, (B, T, R), "zt")
+    _shape(Ug, (H, dk, R), "Ug")
+    _shape(Ut, (H, dk, R), "Ut")
+    _shape(bg, (H, dk), "bg")
+    _shape(bt, (H, dk), "bt")
+    _shape(S0, (B, H, dk, dv), "S0")
+    _shape(o, (B, H, T, dv), "o")
+    _shape(S_T, (B, H, dk, dv), "S_T")
+    for x, nm in ((bg, "bg"), (bt, "bt"), (S0, "S0"), (S_T, "S_T")):
+        if x is not None and x.dtype != torch.float32:
+            raise TypeError(f"{nm} must be float32")
+    _out_dtype(o, q.dtype, "o")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    need = rodimus_scan_prefill_workspace_bytes(B, H, T, dk, dv, chunk, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().rodimus_scan_prefill_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(zg), _ptr(zt), _ptr(Ug), _ptr(bg),
+                                            _ptr(Ut), _ptr(bt), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, R,
+                                            chunk, dt, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "rodimus_scan_prefill_lowrank")
     return o, S_T
 
 

@@ -170,6 +170,42 @@ int rodimus_scan_prefill_noalloc(const void *q, const void *k, const void *v, co
                              true, stream);
 }
 
+int rodimus_scan_prefill_lowrank(const void *q, const void *k, const void *v, const void *zg,
+                                 const void *zt, const void *Ug, const float *bg, const void *Ut,
+                                 const float *bt, const float *S0, void *o, float *S_T, int B, int H,
+                                 int T, int dk, int dv, int rank, int chunk, int dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    if (!scan_sizes_ok(B, H, T, dk, dv, chunk, dtype) || rank <= 0) return RODIMUS_ERR_INVALID_ARG;
+    if (!ok_opt_ptr(S0) || !ok_opt_ptr(S_T) || !ok_opt_ptr(workspace)) return RODIMUS_ERR_INVALID_ARG;
+    if (S0 && S_T && S0 == S_T) return RODIMUS_ERR_INVALID_ARG;
+    if (chunk == 0) chunk = 64;
+    if (dtype != RODIMUS_BF16 || dk != 128 || dv != 128 || rank != 16 || (chunk != 32 && chunk != 64))
+        return RODIMUS_ERR_UNSUPPORTED;
+    if ((long long)T * 32 >= (1LL << 31)) return RODIMUS_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (B == 0 || H == 0) return RODIMUS_OK;
+    if (T == 0) {
+        if (S_T) {
+            launch_state_copy(S0, S_T, (size_t)B * H * dk * dv, st);
+            return hip_status();
+        }
+        return RODIMUS_OK;
+    }
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(zg) || !ok_ptr(zt) || !ok_ptr(Ug) || !ok_ptr(Ut) ||
+        !ok_ptr(bg) || !ok_ptr(bt) || !ok_ptr(o))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanPlan plan = plan_scan(B, H, T, dk, dv, chunk, dtype);
+    if (!plan.mfma) return RODIMUS_ERR_UNSUPPORTED;
+    if (!scan_launch_fits(plan, B, H, T, chunk)) return RODIMUS_ERR_INVALID_ARG;
+    if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+        return RODIMUS_ERR_INVALID_ARG;
+    ScanArgs a{q, k, v, nullptr, nullptr, S0, o, S_T, B, H, T, dk, dv, chunk, dtype, workspace,
+               workspace_bytes};
+    a.zg = zg; a.zt = zt; a.Ug = Ug; a.Ut = Ut; a.bg = bg; a.bt = bt;
+    launch_scan_mfma(a, plan, st);
+    return hip_status();
+}
+
 size_t rodimus_scan_prefill_varlen_workspace_bytes(int N, int H, int max_seqlen, int dk, int dv,
                                                    int chunk, int dtype) {
     if (!scan_sizes_ok(N, H, max_seqlen, dk, dv, chunk, dtype)) return 0;

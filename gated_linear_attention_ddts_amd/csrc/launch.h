@@ -20,6 +20,11 @@ struct ScanArgs {
     const int *cu = nullptr;
     int total = 0;
     int *order = nullptr;
+    // low-rank gates (nullable; batched layout, bf16, dk = dv = 128 only): the
+    // rank-16 factor rows zg, zt [B][T][16] replace g and tau; Ug, Ut
+    // [H][128][16] bf16 and bg, bt [H][128] fp32 are the per-head factors
+    const void *zg = nullptr, *zt = nullptr, *Ug = nullptr, *Ut = nullptr;
+    const float *bg = nullptr, *bt = nullptr;
 };
 
 struct ScanBwdArgs {

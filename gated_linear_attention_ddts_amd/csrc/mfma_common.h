@@ -93,28 +93,52 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
 // Producer lane (256 of them): channel group cg (channels 8cg..8cg+7) and
 // token group r (tokens TPR*r .. TPR*r+TPR-1); the 16 lanes of a DPP row
 // share cg and together cover the C tokens of the chunk.
-template <int C, bool WITH_Q>
+// LR: the gate inputs come separately (Zops); g and th are then unused.
+template <int C, bool WITH_Q, bool LR = false>
 struct Raw {
-    static constexpr int TPR = C / 16;
-    uint4 q[WITH_Q ? TPR : 1], k[TPR], g[TPR], th[TPR], v[TPR];
+    static constexpr int TPR = C / 16, NG = LR ? 1 : TPR;
+    uint4 q[WITH_Q ? TPR : 1], k[TPR], g[NG], th[NG], v[TPR];
 };
 
 struct Rsrc {
     __amdgpu_buffer_rsrc_t q, k, v, g, th;
 };
 
+// Rank of the low-rank gate factors, and the bytes of one factor row.
+constexpr int kRank = 16;
+constexpr uint32_t kZRow = kRank * 2;
+
+// Descriptor over `bytes` bytes (reads past the end return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_bytes(const bf16_t *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)uni_ptr(base), (short)0, uni(bytes), 0x00020000);
+}
+
 // Loads past T read zeros (buffer bounds).
-template <int C, bool WITH_Q>
-__device__ __forceinline__ void load_raw(Raw<C, WITH_Q> &R, const Rsrc &rs, int t0, int r, int cg) {
+template <int C, bool WITH_Q, bool LR>
+__device__ __forceinline__ void load_raw(Raw<C, WITH_Q, LR> &R, const Rsrc &rs, int t0, int r, int cg) {
     constexpr int TPR = C / 16;
 #pragma unroll
     for (int tt = 0; tt < TPR; ++tt) {
         const uint32_t off = (uint32_t)(t0 + TPR * r + tt) * (kD * 2u) + 16u * cg;
         if (WITH_Q) R.q[tt] = bload(rs.q, off);
         R.k[tt] = bload(rs.k, off);
+        if (!LR) {
+            R.g[tt] = bload(rs.g, off);
+            R.th[tt] = bload(rs.th, off);
+        }
+        R.v[tt] = bload(rs.v, off);
+    }
+}
+
+// Next chunk's gate-logit rows.
+template <int C, bool WITH_Q, bool LR>
+__device__ __forceinline__ void load_gates(Raw<C, WITH_Q, LR> &R, const Rsrc &rs, int t0, int r, int cg) {
+    constexpr int TPR = C / 16;
+#pragma unroll
+    for (int tt = 0; tt < TPR; ++tt) {
+        const uint32_t off = (uint32_t)(t0 + TPR * r + tt) * (kD * 2u) + 16u * cg;
         R.g[tt] = bload(rs.g, off);
         R.th[tt] = bload(rs.th, off);
-        R.v[tt] = bload(rs.v, off);
     }
 }
 
@@ -126,22 +150,111 @@ __device__ __forceinline__ void load_one(uint4 (&x)[TPR], __amdgpu_buffer_rsrc_t
     for (int tt = 0; tt < TPR; ++tt) x[tt] = bload(rs, (uint32_t)(t0 + TPR * r + tt) * (kD * 2u) + 16u * cg);
 }
 
-// Gates and in-chunk inclusive scan: on return l2a holds Lam (inclusive
-// cumulative log2 a), l2b log2 beta, lend the chunk total Lam[C-1] of each of
-// the lane's 8 channels.  Tokens at or beyond tend get a = 1, beta = 0.
-template <int C>
-__device__ __forceinline__ void gates_scan_gt(const uint4 (&G)[C / 16], const uint4 (&TH)[C / 16], int t0,
-                                              int tend, int r, int l, float (&l2a)[C / 16][8],
-                                              float (&l2b)[C / 16][8], float (&lend)[8]) {
-    constexpr int TPR = C / 16;
+// ------------------------------------------------- low-rank gate factors
+// The gate logits of a chunk from rank-16 factor rows on the matrix cores.
+// Producer wave w owns key channels 32w..32w+31; per 32-token tile and gate,
+//     G[t][c] = silu(Z_g[t][:]) . U_g[c][:] + b_g[c]       (tau: no silu)
+// is one v_mfma_f32_32x32x16_bf16 with A = the tile's factor rows (lane
+// m + 32*(k/8): token m, ranks 8(k/8)..+7, one 16-byte load), B = U^T (lane
+// n + 32*(k/8): channel 32w+n, same ranks, held for the whole kernel) and the
+// accumulator initialised with the bias (one value per lane: channel n).  The
+// wave writes the bf16 logits into its own 32 channel rows of an LDS area
+// laid out [channel][token] (rows of ROW bf16), then each lane reads back its
+// channels and tokens in the producer layout.
+struct LrOps {
+    bf16x8_t ug, ut;    // B operands
+    float bg, bt;       // biases of channel 32w + (lane & 31)
+};
+
+__device__ __forceinline__ void lr_load_ops(LrOps &o, const bf16_t *Ug, const float *bg, const bf16_t *Ut,
+                                            const float *bt, int h, int w, int l) {
+    const size_t c = (size_t)h * kD + 32 * w + (l & 31);
+    o.ug = *reinterpret_cast<const bf16x8_t *>(Ug + c * kRank + 8 * (l >> 5));
+    o.ut = *reinterpret_cast<const bf16x8_t *>(Ut + c * kRank + 8 * (l >> 5));
+    o.bg = bg[c];
+    o.bt = bt[c];
+}
+
+// A-operand factor rows of NTL 32-token tiles starting at token t0 (rows past
+// the descriptor's end read zeros).
+template <int NTL>
+struct Zops {
+    uint4 g[NTL], t[NTL];
+};
+
+template <int NTL>
+__device__ __forceinline__ void load_zops(Zops<NTL> &z, __amdgpu_buffer_rsrc_t rg, __amdgpu_buffer_rsrc_t rt, int t0,
+                                          int l) {
 #pragma unroll
-    for (int tt = 0; tt < TPR; ++tt) {
-        float gf[8], tf[8];
-        unpack8(G[tt], gf);
-        unpack8(TH[tt], tf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ddts_log2_gates_fast(gf[e], tf[e], l2a[tt][e], l2b[tt][e]);
+    for (int tl = 0; tl < NTL; ++tl) {
+        const uint32_t off = (uint32_t)(t0 + 32 * tl + (l & 31)) * kZRow + 16u * (l >> 5);
+        z.g[tl] = bload(rg, off);
+        z.t[tl] = bload(rt, off);
     }
+}
+
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.f + exp2_fast(-x * kLog2e));
+}
+
+// silu of 8 bf16 values, rounded back to bf16 (the operand precision).
+__device__ __forceinline__ bf16x8_t silu8(const uint4 &x) {
+    float f[8];
+    unpack8(x, f);
+    const uint4 u = make_uint4(pack2(silu(f[0]), silu(f[1])), pack2(silu(f[2]), silu(f[3])),
+                               pack2(silu(f[4]), silu(f[5])), pack2(silu(f[6]), silu(f[7])));
+    return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Logits of the NTL tiles into the wave's rows 32w..32w+31 of sg (g) and st
+// (tau), token columns 0..32*NTL-1.
+template <int NTL, int ROW>
+__device__ __forceinline__ void lr_stage(const Zops<NTL> &z, const LrOps &o, char *sg, char *st, int w, int l) {
+    const int n = l & 31, hh = l >> 5;
+#pragma unroll
+    for (int tl = 0; tl < NTL; ++tl) {
+#pragma unroll
+        for (int gate = 0; gate < 2; ++gate) {
+            const float b = gate ? o.bt : o.bg;
+            f32x16_t acc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = b;
+            const bf16x8_t a = gate ? __builtin_bit_cast(bf16x8_t, z.t[tl]) : silu8(z.g[tl]);
+            acc = mfma(a, gate ? o.ut : o.ug, acc);
+            char *row = (gate ? st : sg) + ((32 * w + n) * ROW + 32 * tl + 4 * hh) * 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint2 *>(row + 16 * j) =
+                    make_uint2(pack2(acc[4 * j], acc[4 * j + 1]), pack2(acc[4 * j + 2], acc[4 * j + 3]));
+        }
+    }
+}
+
+// Producer lane (r, cg): the staged logits of its channels 8cg..8cg+7 and
+// tokens TPR*r.., as TPR/2 words (two tokens each) per channel.
+template <int TPR, int ROW>
+__device__ __forceinline__ void lr_read(const char *sg, const char *st, int r, int cg,
+                                        uint32_t (&gw)[8][TPR / 2], uint32_t (&tw)[8][TPR / 2]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int off = ((8 * cg + e) * ROW + TPR * r) * 2;
+        if constexpr (TPR == 4) {
+            const uint2 a = *reinterpret_cast<const uint2 *>(sg + off), b = *reinterpret_cast<const uint2 *>(st + off);
+            gw[e][0] = a.x; gw[e][1] = a.y; tw[e][0] = b.x; tw[e][1] = b.y;
+        } else {
+            gw[e][0] = *reinterpret_cast<const uint32_t *>(sg + off);
+            tw[e][0] = *reinterpret_cast<const uint32_t *>(st + off);
+        }
+    }
+}
+
+// In-chunk inclusive scan of log2 a (l2a on entry): on return l2a holds Lam
+// (inclusive cumulative log2 a), lend the chunk total Lam[C-1] of each of the
+// lane's 8 channels.  Tokens at or beyond tend get a = 1, beta = 0.
+template <int C>
+__device__ __forceinline__ void chunk_scan(int t0, int tend, int r, int l, float (&l2a)[C / 16][8],
+                                           float (&l2b)[C / 16][8], float (&lend)[8]) {
+    constexpr int TPR = C / 16;
     if (t0 + C > tend) {  // ragged last chunk
 #pragma unroll
         for (int tt = 0; tt < TPR; ++tt)
@@ -168,11 +281,48 @@ __device__ __forceinline__ void gates_scan_gt(const uint4 (&G)[C / 16], const ui
     }
 }
 
-template <int C, bool WITH_Q>
-__device__ __forceinline__ void gates_scan(const Raw<C, WITH_Q> &R, int t0, int tend, int r, int l,
-                                           float (&l2a)[C / 16][8], float (&l2b)[C / 16][8],
-                                           float (&lend)[8]) {
-    gates_scan_gt<C>(R.g, R.th, t0, tend, r, l, l2a, l2b, lend);
+// Gates and in-chunk inclusive scan: on return l2a holds Lam (inclusive
+// cumulative log2 a), l2b log2 beta, lend the chunk total Lam[C-1] of each of
+// the lane's 8 channels.  Tokens at or beyond tend get a = 1, beta = 0.
+template <int C>
+__device__ __forceinline__ void gates_scan_gt(const uint4 (&G)[C / 16], const uint4 (&TH)[C / 16], int t0,
+                                              int tend, int r, int l, float (&l2a)[C / 16][8],
+                                              float (&l2b)[C / 16][8], float (&lend)[8]) {
+    constexpr int TPR = C / 16;
+#pragma unroll
+    for (int tt = 0; tt < TPR; ++tt) {
+        float gf[8], tf[8];
+        unpack8(G[tt], gf);
+        unpack8(TH[tt], tf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ddts_log2_gates_fast(gf[e], tf[e], l2a[tt][e], l2b[tt][e]);
+    }
+    chunk_scan<C>(t0, tend, r, l, l2a, l2b, lend);
+}
+
+// The same from logits staged per channel (lr_read's words).
+template <int C>
+__device__ __forceinline__ void gates_scan_cols(const uint32_t (&gw)[8][C / 32], const uint32_t (&tw)[8][C / 32],
+                                                int t0, int tend, int r, int l, float (&l2a)[C / 16][8],
+                                                float (&l2b)[C / 16][8], float (&lend)[8]) {
+    constexpr int TPR = C / 16;
+#pragma unroll
+    for (int tt = 0; tt < TPR; ++tt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t gu = gw[e][tt >> 1], tu = tw[e][tt >> 1];
+            const float gv = (tt & 1) ? hi_bf(gu) : lo_bf(gu), tv = (tt & 1) ? hi_bf(tu) : lo_bf(tu);
+            ddts_log2_gates_fast(gv, tv, l2a[tt][e], l2b[tt][e]);
+        }
+    chunk_scan<C>(t0, tend, r, l, l2a, l2b, lend);
+}
+
+// Forces the raw registers of a chunk to have arrived here (an empty asm that
+// reads them), before the next chunk's prefetches are issued: a wait placed
+// after those prefetches would, with the in-order load counter, wait for them
+// too and expose a whole memory latency per chunk.
+__device__ __forceinline__ void arrived(const uint4 &x) {
+    __asm__ volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
 }
 
 // Row c of Kb^T / V^T: tokens TPR*r .. TPR*r+TPR-1 at their permuted position.

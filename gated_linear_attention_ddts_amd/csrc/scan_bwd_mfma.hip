@@ -161,7 +161,7 @@ void bwd_state_kernel(P p) {
 
         // operands: X^T (Kb or Qt) and Y^T (V or dO), tokens in permuted order
         float l2a[2][8], l2b[2][8], lend[8];
-        gates_scan<kStS, false>(R, t0, len, r, l, l2a, l2b, lend);
+        gates_scan_gt<kStS>(R.g, R.th, t0, len, r, l, l2a, l2b, lend);
         float xT[8][2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {

@@ -87,6 +87,11 @@ struct Params {
     const int *cu;
     int H, total;
     const int *order;  // packed batch: longest-first order of the sequences, or null
+    // low-rank gates (LR kernels): factor rows zg, zt [B][T][16] bf16 shared by
+    // the heads; per-head factors Ug, Ut [H][128][16] bf16 and biases bg, bt
+    // [H][128] fp32
+    const bf16_t *zg, *zt, *Ug, *Ut;
+    const float *bg, *bt;
 };
 
 // Rows of (b,h): first row and length.  The packed form clamps each span to
@@ -106,8 +111,24 @@ __device__ __forceinline__ void seq_span(const Params &p, int bh, size_t &rowbas
     len = min(b - a, p.T);
 }
 
+// The four consumer waves meet (an LDS counter; the producer waves are not
+// involved), with a bounded wait.  Returns true if the wait gave up: what the
+// other waves wrote may then be stale, and the caller poisons its outputs.
+__device__ __forceinline__ bool consumer_barrier(int *sCBar, int &target, int l) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (l == 0) __hip_atomic_fetch_add(sCBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    target += 4;
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+        if (__hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    const bool stale = __hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    return stale;
+}
+
 // ------------------------------------------------------------- phase 3 (full)
-template <int C, bool VL>
+template <int C, bool VL, bool LR>
 __global__ __launch_bounds__(512, 1)
 void scan_full_kernel(Params p) {
     constexpr int TPR = C / 16, NT = C / 32;
@@ -135,22 +156,53 @@ void scan_full_kernel(Params p) {
         const int r = l & 15, cg = (w << 2) | (l >> 4);
         Rsrc rs;
         rs.q = rsrc(p.q + rowbase * kD, Tb); rs.k = rsrc(p.k + rowbase * kD, Tb);
-        rs.v = rsrc(p.v + rowbase * kD, Tb); rs.g = rsrc(p.g + rowbase * kD, Tb);
-        rs.th = rsrc(p.th + rowbase * kD, Tb);
-        Raw<C, true> R;
+        rs.v = rsrc(p.v + rowbase * kD, Tb);
+        // low-rank gates: factor-row descriptors, the head's factors (B
+        // operands) and the first chunk's factor rows
+        __amdgpu_buffer_rsrc_t rzg, rzt;
+        LrOps ops;
+        Zops<NT> Z;
+        if constexpr (LR) {
+            const size_t zrow = (size_t)(bh / p.H) * p.T;
+            rzg = rsrc_bytes(p.zg + zrow * kRank, Tb * (int)kZRow);
+            rzt = rsrc_bytes(p.zt + zrow * kRank, Tb * (int)kZRow);
+            lr_load_ops(ops, p.Ug, p.bg, p.Ut, p.bt, bh % p.H, w, l);
+            load_zops<NT>(Z, rzg, rzt, t_begin, l);
+        } else {
+            rs.g = rsrc(p.g + rowbase * kD, Tb);
+            rs.th = rsrc(p.th + rowbase * kD, Tb);
+        }
+        Raw<C, true, LR> R;
         load_raw<C, true>(R, rs, t_begin, r, cg);
         for (int kk = 0; kk <= nch; ++kk) {
             if (kk < nch) {
                 const int t0 = t_begin + kk * C;
                 char *buf = smem + (kk & 1) * kBufBytes;
                 const bool more = kk + 1 < nch;
-                store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);
-                if (more) load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
                 float l2a[TPR][8], l2b[TPR][8], lend[8];
-                gates_scan<C, true>(R, t0, t_end, r, l, l2a, l2b, lend);
-                if (more) {
-                    load_one<TPR>(R.g, rs.g, t0 + C, r, cg);
-                    load_one<TPR>(R.th, rs.th, t0 + C, r, cg);
+                if constexpr (LR) {
+                    // every raw input of this chunk has arrived before any
+                    // prefetch of the next one is issued
+#pragma unroll
+                    for (int tt = 0; tt < TPR; ++tt) { arrived(R.q[tt]); arrived(R.k[tt]); arrived(R.v[tt]); }
+                    // logits on the matrix cores, staged in this wave's rows of
+                    // the K-bar^T (g) and V^T (tau) areas, read back per lane
+                    lr_stage<NT, kTRow>(Z, ops, buf + kOffKbT, buf + kOffVT, w, l);
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    uint32_t gw[8][TPR / 2], tw[8][TPR / 2];
+                    lr_read<TPR, kTRow>(buf + kOffKbT, buf + kOffVT, r, cg, gw, tw);
+                    store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);   // after the reads, in LDS order
+                    if (more) {
+                        load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
+                        load_zops<NT>(Z, rzg, rzt, t0 + C, l);
+                    }
+                    gates_scan_cols<C>(gw, tw, t0, t_end, r, l, l2a, l2b, lend);
+                } else {
+                    store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);
+                    if (more) load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
+                    gates_scan_gt<C>(R.g, R.th, t0, t_end, r, l, l2a, l2b, lend);
+                    if (more) load_gates<C, true>(R, rs, t0 + C, r, cg);
                 }
                 bool bad = false;
                 float gam[8];
@@ -222,26 +274,75 @@ void scan_full_kernel(Params p) {
                 float *fa = reinterpret_cast<float *>(buf) + cw * 1536;  // [4][128] a
                 float *fb = fa + 512;                                    // [4][128] beta*k
                 float *fq = fb + 512;                                    // [4][128] q
-                for (int sb = 0; sb < C; sb += 4) {
-                    for (int e = l; e < 512; e += 64) {
-                        const int tt = e >> 7, i = e & 127, t = t0 + sb + tt;
+                bool fstale = false;
+                if constexpr (LR) {
+                    // The chunk's gate logits, recomputed on the matrix cores as the
+                    // producers do (consumer wave cw: channels 32cw..32cw+31) into the
+                    // K-bar^T (g) and V^T (tau) areas, which the fallback leaves unused.
+                    const size_t zrow = (size_t)(bh / p.H) * p.T;
+                    LrOps cops;
+                    Zops<NT> cz;
+                    lr_load_ops(cops, p.Ug, p.bg, p.Ut, p.bt, bh % p.H, cw, l);
+                    load_zops<NT>(cz, rsrc_bytes(p.zg + zrow * kRank, Tb * (int)kZRow),
+                                  rsrc_bytes(p.zt + zrow * kRank, Tb * (int)kZRow), t0, l);
+                    lr_stage<NT, kTRow>(cz, cops, buf + kOffKbT, buf + kOffVT, cw, l);
+                    fstale = consumer_barrier(sCBar, cbar_target, l);
+                }
+                // The inputs of each 4-token sub-block (element k of the lane: token
+                // k >> 1, channel l + 64 (k & 1); v of its column n for the 4 tokens)
+                // are loaded in one batch: one memory round trip per sub-block.
+                struct FallRaw {
+                    bf16_t g[8], th[8], k[8], q[8], v[4];
+                };
+                auto fall_load = [&](FallRaw &R, int sb) {
+#pragma unroll
+                    for (int k8 = 0; k8 < 8; ++k8) {
+                        const int t = t0 + sb + (k8 >> 1);
+                        if (t < t_end) {
+                            const size_t x = (rowbase + t) * kD + l + 64 * (k8 & 1);
+                            if constexpr (!LR) {
+                                R.g[k8] = p.g[x];
+                                R.th[k8] = p.th[x];
+                            }
+                            R.k[k8] = p.k[x];
+                            R.q[k8] = p.q[x];
+                        }
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        if (t0 + sb + tt < t_end) R.v[tt] = p.v[(rowbase + t0 + sb + tt) * kD + n];
+                };
+                auto fall_sub = [&](int sb) {
+                    FallRaw R;
+                    fall_load(R, sb);
+#pragma unroll
+                    for (int k8 = 0; k8 < 8; ++k8) {
+                        const int tt = k8 >> 1, i = l + 64 * (k8 & 1), e = tt * 128 + i, t = t0 + sb + tt;
                         float a = 1.f, bk = 0.f, qq = 0.f;
                         if (t < t_end) {
-                            const size_t x = (rowbase + t) * kD + i;
-                            float l2a, l2b;
-                            ddts_log2_gates(bf2f(p.g[x]), bf2f(p.th[x]), l2a, l2b);
+                            float gv, tv, l2a, l2b;
+                            if constexpr (LR) {
+                                const int so = (i * kTRow + sb + tt) * 2;
+                                gv = bf2f(*reinterpret_cast<const bf16_t *>(buf + kOffKbT + so));
+                                tv = bf2f(*reinterpret_cast<const bf16_t *>(buf + kOffVT + so));
+                            } else {
+                                gv = bf2f(R.g[k8]);
+                                tv = bf2f(R.th[k8]);
+                            }
+                            ddts_log2_gates(gv, tv, l2a, l2b);
                             a = exp2_fast(l2a);
-                            bk = exp2_fast(l2b) * bf2f(p.k[x]);
-                            qq = bf2f(p.q[x]);
+                            bk = exp2_fast(l2b) * bf2f(R.k[k8]);
+                            qq = bf2f(R.q[k8]);
                         }
                         fa[e] = a; fb[e] = bk; fq[e] = qq;
                     }
                     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                     __builtin_amdgcn_wave_barrier();
+#pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
                         const int t = t0 + sb + tt;
-                        if (t >= t_end) break;
-                        const float vn = bf2f(p.v[(rowbase + t) * kD + n]);
+                        if (t >= t_end) continue;
+                        const float vn = bf2f(R.v[tt]);
                         float part = 0.f;
 #pragma unroll
                         for (int mt = 0; mt < 4; ++mt) {
@@ -268,11 +369,12 @@ void scan_full_kernel(Params p) {
                             __builtin_amdgcn_sched_barrier(0);
                         }
                         part += __shfl_xor(part, 32);
-                        if (h == 0) p.o[(rowbase + t) * kD + n] = f2bf(part);
+                        if (h == 0) p.o[(rowbase + t) * kD + n] = fstale ? (bf16_t)0x7fc0 : f2bf(part);
                     }
                     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                     __builtin_amdgcn_wave_barrier();
-                }
+                };
+                for (int sb = 0; sb < C; sb += 4) fall_sub(sb);
             } else {
                 // V^T fragments: B operand (k = token, permuted order) of both
                 // o += A V and S += Kb^T V
@@ -309,20 +411,10 @@ void scan_full_kernel(Params p) {
                             make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
                     }
                 }
-                // the four consumer waves meet (LDS counter; the producer waves are
-                // not involved); bounded wait
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                if (l == 0) __hip_atomic_fetch_add(sCBar, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                cbar_target += 4;
-                for (int spin = 0; spin < (1 << 24); ++spin) {
-                    if (__hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= cbar_target) break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                // a wait that gave up leaves score tiles that may be stale: this
-                // chunk's outputs are then written as NaN, never as silent garbage
-                const bool stale =
-                    __hip_atomic_load(sCBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < cbar_target;
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                // the four consumer waves meet; a wait that gave up leaves score
+                // tiles that may be stale: this chunk's outputs are then written as
+                // NaN, never as silent garbage
+                const bool stale = consumer_barrier(sCBar, cbar_target, l);
                 // o^T tiles: 32 value channels (this wave's) x 32 tokens (32It..).  Same
                 // fragments as o = Qt S + A V with the operands swapped, so that a
                 // lane holds one token and 4 consecutive channels per register group.
@@ -380,17 +472,33 @@ void scan_full_kernel(Params p) {
 // One sub-segment's local end state.  Processed in chunks of 32 tokens whatever
 // the caller's C (the result does not depend on the chunking), which leaves
 // room in the registers for two chunks of raw inputs in flight.
-template <int TPR>
-__device__ __forceinline__ void state_chunk(Raw<16 * TPR, false> &R, const Rsrc &rs, int t0, int tnext,
-                                            char *sKbT, char *sVT, f32x16_t (&S)[4], float (&rho)[8],
-                                            int r, int cg, int l, int w, int h, int l32, int T) {
-    store_vt<TPR, kTRow>(sVT, cg, r, R.v);
-    if (tnext >= 0) load_one<TPR>(R.v, rs.v, tnext, r, cg);
+template <int TPR, bool LR>
+__device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1> &Z, const LrOps &ops,
+                                            __amdgpu_buffer_rsrc_t rzg, __amdgpu_buffer_rsrc_t rzt, const Rsrc &rs,
+                                            int t0, int tnext, char *sKbT, char *sVT, f32x16_t (&S)[4],
+                                            float (&rho)[8], int r, int cg, int l, int w, int h, int l32, int T) {
     float l2a[TPR][8], l2b[TPR][8], lend[8];
-    gates_scan<16 * TPR, false>(R, t0, T, r, l, l2a, l2b, lend);
-    if (tnext >= 0) {
-        load_one<TPR>(R.g, rs.g, tnext, r, cg);
-        load_one<TPR>(R.th, rs.th, tnext, r, cg);
+    if constexpr (LR) {
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) { arrived(R.k[tt]); arrived(R.v[tt]); }
+        // logits of the 32-token chunk on the matrix cores, staged in this
+        // wave's rows of the K-bar^T (g) and V^T (tau) areas
+        lr_stage<1, kTRow>(Z, ops, sKbT, sVT, w, l);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t gw[8][TPR / 2], tw[8][TPR / 2];
+        lr_read<TPR, kTRow>(sKbT, sVT, r, cg, gw, tw);
+        store_vt<TPR, kTRow>(sVT, cg, r, R.v);   // after the reads, in LDS order
+        if (tnext >= 0) {
+            load_one<TPR>(R.v, rs.v, tnext, r, cg);
+            load_zops<1>(Z, rzg, rzt, tnext, l);
+        }
+        gates_scan_cols<16 * TPR>(gw, tw, t0, T, r, l, l2a, l2b, lend);
+    } else {
+        store_vt<TPR, kTRow>(sVT, cg, r, R.v);
+        if (tnext >= 0) load_one<TPR>(R.v, rs.v, tnext, r, cg);
+        gates_scan_gt<16 * TPR>(R.g, R.th, t0, T, r, l, l2a, l2b, lend);
+        if (tnext >= 0) load_gates<16 * TPR, false>(R, rs, tnext, r, cg);
     }
     float kbT[8][TPR];
 #pragma unroll
@@ -418,7 +526,7 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false> &R, const Rsrc 
     __syncthreads();
 }
 
-template <bool VL>
+template <bool VL, bool LR>
 __global__ __launch_bounds__(256, 2)
 void scan_state_kernel(Params p) {
     constexpr int CS = 32, TPR = CS / 16;
@@ -443,7 +551,17 @@ void scan_state_kernel(Params p) {
 
     Rsrc rs;
     rs.k = rsrc(p.k + rowbase * kD, Tb); rs.v = rsrc(p.v + rowbase * kD, Tb);
-    rs.g = rsrc(p.g + rowbase * kD, Tb); rs.th = rsrc(p.th + rowbase * kD, Tb);
+    __amdgpu_buffer_rsrc_t rzg, rzt;
+    LrOps ops;
+    if constexpr (LR) {
+        const size_t zrow = (size_t)(bh / p.H) * p.T;
+        rzg = rsrc_bytes(p.zg + zrow * kRank, Tb * (int)kZRow);
+        rzt = rsrc_bytes(p.zt + zrow * kRank, Tb * (int)kZRow);
+        lr_load_ops(ops, p.Ug, p.bg, p.Ut, p.bt, bh % p.H, w, l);
+    } else {
+        rs.g = rsrc(p.g + rowbase * kD, Tb);
+        rs.th = rsrc(p.th + rowbase * kD, Tb);
+    }
     rs.q = rs.k;
 
     f32x16_t S[4];
@@ -454,16 +572,23 @@ void scan_state_kernel(Params p) {
     for (int e = 0; e < 8; ++e) rho[e] = 0.f;
 
     // chunks are visited last to first; two chunks of raw inputs are in flight
-    Raw<CS, false> Ra, Rb;
+    Raw<CS, false, LR> Ra, Rb;
+    Zops<1> Za, Zb;
     const int c0 = nch - 1;
-    if (c0 >= 0) load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
-    if (c0 >= 1) load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
+    if (c0 >= 0) {
+        load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
+        if constexpr (LR) load_zops<1>(Za, rzg, rzt, t_begin + c0 * CS, l);
+    }
+    if (c0 >= 1) {
+        load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
+        if constexpr (LR) load_zops<1>(Zb, rzg, rzt, t_begin + (c0 - 1) * CS, l);
+    }
     for (int c = c0; c >= 0; c -= 2) {
-        state_chunk<TPR>(Ra, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1, sKbT, sVT,
-                         S, rho, r, cg, l, w, h, l32, Tb);
-        if (c >= 1)
-            state_chunk<TPR>(Rb, rs, t_begin + (c - 1) * CS, c >= 3 ? t_begin + (c - 3) * CS : -1,
+        state_chunk<TPR, LR>(Ra, Za, ops, rzg, rzt, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1,
                              sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
+        if (c >= 1)
+            state_chunk<TPR, LR>(Rb, Zb, ops, rzg, rzt, rs, t_begin + (c - 1) * CS,
+                                 c >= 3 ? t_begin + (c - 3) * CS : -1, sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
     }
     float *So = p.wsS + ((size_t)sub * p.BH + bh) * kD * kD;
 #pragma unroll
@@ -586,21 +711,27 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.sub_len = q.sub * a.chunk;
     p.cu = a.cu; p.H = a.H; p.total = a.total;
     p.order = a.cu ? a.order : nullptr;
-    const bool vl = a.cu != nullptr;
+    p.zg = (const bf16_t *)a.zg; p.zt = (const bf16_t *)a.zt;
+    p.Ug = (const bf16_t *)a.Ug; p.Ut = (const bf16_t *)a.Ut; p.bg = a.bg; p.bt = a.bt;
+    const bool vl = a.cu != nullptr, lr = a.zg != nullptr;
     if (q.G > 1) {
-        if (vl) hipLaunchKernelGGL(scan_state_kernel<true>, dim3(nsub * BH), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL(scan_state_kernel<false>, dim3(nsub * BH), dim3(256), 0, st, p);
+        const dim3 g1(nsub * BH), b1(256);
+        if (lr) hipLaunchKernelGGL((scan_state_kernel<false, true>), g1, b1, 0, st, p);
+        else if (vl) hipLaunchKernelGGL((scan_state_kernel<true, false>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((scan_state_kernel<false, false>), g1, b1, 0, st, p);
         const size_t n4 = (size_t)BH * kD * kD / 4;
         hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
                            a.S0, p.wsS, p.wsA, BH, nsub, q.P);
     }
     const dim3 grid(q.G * BH), blk(512);
     if (a.chunk == 64) {
-        if (vl) hipLaunchKernelGGL((scan_full_kernel<64, true>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((scan_full_kernel<64, false>), grid, blk, 0, st, p);
+        if (lr) hipLaunchKernelGGL((scan_full_kernel<64, false, true>), grid, blk, 0, st, p);
+        else if (vl) hipLaunchKernelGGL((scan_full_kernel<64, true, false>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((scan_full_kernel<64, false, false>), grid, blk, 0, st, p);
     } else {
-        if (vl) hipLaunchKernelGGL((scan_full_kernel<32, true>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((scan_full_kernel<32, false>), grid, blk, 0, st, p);
+        if (lr) hipLaunchKernelGGL((scan_full_kernel<32, false, true>), grid, blk, 0, st, p);
+        else if (vl) hipLaunchKernelGGL((scan_full_kernel<32, true, false>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((scan_full_kernel<32, false, false>), grid, blk, 0, st, p);
     }
 }
 

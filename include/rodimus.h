@@ -7,7 +7,9 @@
  *
  *  rodimus_scan_prefill  the DDTS-gated linear-attention recurrence over a
  *                        whole prompt, in chunkwise-parallel form (also over
- *                        a packed batch of ragged sequences, _varlen);
+ *                        a packed batch of ragged sequences, _varlen, and with
+ *                        the gate logits expanded in-kernel from low-rank
+ *                        factors, _lowrank);
  *  rodimus_scan_backward its gradients with respect to every input (also
  *                        over the packed batch, _varlen);
  *  rodimus_decode_step   one recurrent step on a resident fixed-size state;
@@ -125,6 +127,46 @@ int rodimus_scan_prefill(const void *q, const void *k, const void *v, const void
                          const void *tau, const float *S0, void *o, float *S_T,
                          int B, int H, int T, int dk, int dv, int chunk, int dtype,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * rodimus_scan_prefill with the gate logits produced inside the kernels from
+ * low-rank factors, so that g and tau ([B,H,T,dk] each, a third of the
+ * prefill's input bytes) never pass through device memory.  The CodeFuse
+ * article's Rodimus block paragraph computes the selection and temperature
+ * gates from the token through learnable weights, and the module
+ * configuration in section 3 of the Rodimus* deployment blog names SiLU as
+ * the selection gate's activation; neither page prints the projection.  The
+ * reading computed here: each token's hidden state is projected (outside this
+ * library, e.g. as extra output columns of the q/k/v projection) to two
+ * rank-R factor rows z_g, z_tau shared by all heads, and per head h and key
+ * channel c
+ *
+ *     g[b,h,t,c]   = sum_r silu(z_g[b,t,r]) * U_g[h,c,r]   + b_g[h,c]
+ *     tau[b,h,t,c] = sum_r      z_tau[b,t,r] * U_tau[h,c,r] + b_tau[h,c]
+ *
+ * then exactly the recurrence of rodimus_scan_prefill.
+ *
+ *   q, k : [B, H, T, dk]    v, o : [B, H, T, dv]         (bf16)
+ *   zg, zt : [B, T, rank]   the factor rows z_g, z_tau   (bf16)
+ *   Ug, Ut : [H, dk, rank]  per-head up-projections      (bf16)
+ *   bg, bt : [H, dk]        per-head biases              (float)
+ *   S0, S_T, chunk, workspace: as for rodimus_scan_prefill, with the same
+ *   workspace size (rodimus_scan_prefill_workspace_bytes with the same B, H,
+ *   T, dk, dv, chunk and dtype).
+ *
+ * Precision: silu(z_g) is rounded to bf16 (the operand precision of this
+ * path) and each logit is accumulated in fp32; everything after that is the
+ * bf16 matrix-core prefill.  Supported: RODIMUS_BF16, dk = dv = 128,
+ * rank = 16, chunk in {32, 64} (0 = 64), T < 2^23 (else
+ * RODIMUS_ERR_UNSUPPORTED; rank <= 0 is RODIMUS_ERR_INVALID_ARG).  Every
+ * pointer except S0, S_T and a NULL workspace must be 16-byte aligned and
+ * non-NULL.  Other rules, launch limits and errors as for rodimus_scan_prefill.
+ */
+int rodimus_scan_prefill_lowrank(const void *q, const void *k, const void *v, const void *zg,
+                                 const void *zt, const void *Ug, const float *bg, const void *Ut,
+                                 const float *bt, const float *S0, void *o, float *S_T, int B, int H,
+                                 int T, int dk, int dv, int rank, int chunk, int dtype, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /*
  * rodimus_scan_prefill without a workspace argument, for callers that cannot

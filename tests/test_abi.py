@@ -369,3 +369,39 @@ def test_scan_noalloc_scratch_covers_every_segment_plan():
                 for bh in (1, 2, 3, 5, 16, 17, 64, 100, 128, 255) for T in (4096, 32704, 131072, 8388607)
                 for c in (32, 64))
     assert worst == 33684480 <= 34 << 20
+
+
+# ------------------------------------------------- prefill with low-rank gates
+def scan_lowrank(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, zg=FAKE, zt=FAKE, Ug=FAKE, bg=FAKE, Ut=FAKE, bt=FAKE, S0=None, o=FAKE,
+             S_T=None, B=1, H=2, T=100, dk=128, dv=128, R=16, chunk=64, dtype=rd.BF16, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return rd.lib().rodimus_scan_prefill_lowrank(a["q"], a["k"], a["v"], a["zg"], a["zt"], a["Ug"], a["bg"],
+                                                 a["Ut"], a["bt"], a["S0"], a["o"], a["S_T"], a["B"], a["H"],
+                                                 a["T"], a["dk"], a["dv"], a["R"], a["chunk"], a["dtype"],
+                                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(v=None), dict(zg=None), dict(zt=None), dict(Ug=None), dict(bg=None), dict(Ut=None),
+    dict(bt=None), dict(o=None), dict(zg=MISALIGNED), dict(bt=MISALIGNED), dict(S0=MISALIGNED),
+    dict(S0=FAKE, S_T=FAKE), dict(B=-1), dict(T=-1), dict(R=0), dict(R=-16), dict(chunk=48), dict(dtype=5),
+    dict(ws=None), dict(ws_bytes=1000),
+    dict(B=1 << 13, H=1 << 10, T=64, ws_bytes=1 << 62),         # grid beyond HIP's limit
+])
+def test_scan_lowrank_rejects(kw):
+    assert scan_lowrank(**kw) == rd.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=rd.F32), dict(dk=64), dict(dv=64), dict(R=8), dict(R=32), dict(chunk=16),
+    dict(T=1 << 23),
+])
+def test_scan_lowrank_unsupported(kw):
+    assert scan_lowrank(**kw) == rd.ERR_UNSUPPORTED
+
+
+def test_scan_lowrank_empty_is_noop():
+    assert scan_lowrank(B=0, q=None) == rd.OK
+    assert scan_lowrank(T=0, q=None, zg=None, o=None) == rd.OK

@@ -91,6 +91,28 @@ def scan_inputs(seed, B, H, T, dk, dv, dtype="bf16", gate_mu=0.0, gate_sigma=1.0
     return dict(q=q, k=k, v=v, g=g, theta=th)
 
 
+def lowrank_inputs(seed, B, H, T, dk, dv, R=16, dtype="bf16", z_sigma=1.0, bias_sigma=0.5, gbias_mu=0.0,
+                   tbias_mu=0.0):
+    """Inputs of the prefill with low-rank gate factors, drawn in this order:
+    q, k, v as scan_inputs (q, k ~ N(0, 1/dk), v ~ N(0, 1)); the factor rows
+    zg, zt [B,T,R] ~ N(0, z_sigma^2); the per-head factors Ug, Ut [H,dk,R]
+    ~ N(0, 1/R) (so each logit has about unit spread); all of those in the
+    storage dtype; then the biases bg ~ N(gbias_mu, bias_sigma^2) and
+    bt ~ N(tbias_mu, bias_sigma^2), [H,dk], fp32."""
+    rng = np.random.default_rng(seed)
+    s = 1.0 / np.sqrt(dk)
+    q = _draw(rng, (B, H, T, dk), 0.0, s, dtype)
+    k = _draw(rng, (B, H, T, dk), 0.0, s, dtype)
+    v = _draw(rng, (B, H, T, dv), 0.0, 1.0, dtype)
+    zg = _draw(rng, (B, T, R), 0.0, z_sigma, dtype)
+    zt = _draw(rng, (B, T, R), 0.0, z_sigma, dtype)
+    Ug = _draw(rng, (H, dk, R), 0.0, 1.0 / np.sqrt(R), dtype)
+    Ut = _draw(rng, (H, dk, R), 0.0, 1.0 / np.sqrt(R), dtype)
+    bg = _draw(rng, (H, dk), gbias_mu, bias_sigma, "fp32")
+    bt = _draw(rng, (H, dk), tbias_mu, bias_sigma, "fp32")
+    return dict(q=q, k=k, v=v, zg=zg, zt=zt, Ug=Ug, Ut=Ut, bg=bg, bt=bt)
+
+
 def decode_pool(seed, N, H, dk, dv, pool=8, dtype="bf16", gate_mu=0.0):
     """``pool`` input sets for the decode step; step s uses set s mod pool."""
     rng = np.random.default_rng(seed)
@@ -179,4 +201,10 @@ CONFIGS = {
     # tokens per head (the token count of the 1.6B batch), 16 heads
     "prefill_varlen_N64_16K": dict(kind="varlen", N=64, H=16, total=16384, min_len=16, dk=128,
                                    dv=128, dtype="bf16", chunk=64, seed=7),
+    # the 1.6B-shaped prefill with the gate logits expanded in-kernel from
+    # rank-16 factor rows shared by the heads (g and tau never stored); the
+    # biases at their initial value 0 (b_tau = 0 is a temperature of 0.5, the
+    # module's tempered_gate_init)
+    "prefill_lowrank_1p6b_T4096": dict(kind="lowrank", B=4, H=16, T=4096, dk=128, dv=128, R=16,
+                                       dtype="bf16", chunk=64, seed=9, bias_sigma=0.0),
 }
