@@ -92,3 +92,37 @@ def test_decode_zero_sizes():
     S = torch.empty(0, 16, 128, 128, device="cuda")
     o = rd.rodimus_decode_step(q, q, q, q, q, S)
     assert o.shape == (0, 16, 128)
+
+
+def test_decode_large_in_place_state_streamed_loads():
+    """An in-place state larger than 640 MiB (N = 704: 738 MB) is read with
+    streaming loads, a smaller one with ordinary loads: both against the
+    oracle on sampled (n, h) pairs, and the large one bitwise equal to the same
+    steps written out of place."""
+    N, H, d, steps = 704, 16, 128, 3
+    log(f"decode N={N} in place ({N * H * d * d * 4 / 1e6:.0f} MB state)")
+    sets = workloads.decode_pool(44, N, H, d, d, pool=steps)
+    S = workloads.device_normal((N, H, d, d), 45).float() * 0.1
+    S_start = host(S)
+    S2 = S.clone()
+    outs_in, outs_out = [], []
+    for s in range(steps):
+        x = {n: dev(sets[s][n]) for n in ("q", "k", "v", "g", "theta")}
+        outs_in.append(rd.rodimus_decode_step(x["q"], x["k"], x["v"], x["g"], x["theta"], S))
+        S_new = torch.empty_like(S2)
+        outs_out.append(rd.rodimus_decode_step(x["q"], x["k"], x["v"], x["g"], x["theta"], S2, S_new))
+        S2 = S_new
+    torch.cuda.synchronize()
+    assert torch.equal(S, S2)
+    for a, b in zip(outs_in, outs_out):
+        assert torch.equal(a, b)
+    pairs = [(0, 0), (351, 7), (703, 15), (511, 3)]
+    ns, hs = [p[0] for p in pairs], [p[1] for p in pairs]
+    Sr = S_start[ns, hs][:, None]
+    for s in range(steps):
+        sub = [sets[s][n].values[ns, hs][:, None].astype(np.float64) for n in ("q", "k", "v", "g", "theta")]
+        ro, Sr = oracle.decode(*sub, Sr)
+        assert err(host(outs_in[s][ns, hs])[:, None], ro) <= TOL["bf16"]
+    e = err(host(S[ns, hs])[:, None], Sr)
+    log(f"  state err on sampled pairs {e:.2e}")
+    assert e <= 1e-4

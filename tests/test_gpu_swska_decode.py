@@ -124,16 +124,17 @@ def test_decode_N64_w4096_sampled_heads():
         assert e <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("N,H,W", [(128, 8, 4100), (512, 1, 4096)])
-def test_long_splits_against_window_oracle(N, H, W):
+@pytest.mark.parametrize("N,H,W,d", [(128, 8, 4100, 128), (512, 1, 4096, 128), (256, 8, 4100, 64),
+                                     (512, 1, 4096, 64)])
+def test_long_splits_against_window_oracle(N, H, W, d):
     # enough (sequence, split, head group) workgroups for the 1024-slot splits
-    # (two heads per workgroup at H = 8, one at H = 1); W = 4100 leaves a
-    # ragged last split; positions from an empty window to several wraps
-    d = 128
-    log(f"swska decode long splits: N={N} H={H} W={W}")
-    kc = workloads.device_normal((N, W, d), 71 + H)
-    vc = workloads.device_normal((N, H, W, d), 72 + H)
-    x = workloads.swska_inputs(73 + H, N, H, 1, d, d)
+    # (two heads per workgroup at H = 8, one at H = 1), at both head sizes;
+    # W = 4100 leaves a ragged last split; positions from an empty window to
+    # several wraps
+    log(f"swska decode long splits: N={N} H={H} W={W} d={d}")
+    kc = workloads.device_normal((N, W, d), 71 + H + d)
+    vc = workloads.device_normal((N, H, W, d), 72 + H + d)
+    x = workloads.swska_inputs(73 + H + d, N, H, 1, d, d)
     qn, kn, vn = dev(x["q"])[:, :, 0].contiguous(), dev(x["k"])[:, 0].contiguous(), dev(x["v"])[:, :, 0].contiguous()
     rng = np.random.default_rng(74 + H)
     ts = rng.integers(0, 3 * W, size=N)
