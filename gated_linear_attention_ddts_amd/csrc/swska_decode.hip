@@ -80,7 +80,7 @@ __device__ __forceinline__ Geo geometry(const int *pos, int n, int W) {
 // together, sums the key slice's dot product with each head's q over the VEC
 // lanes of the row, and folds the rows into a running maximum, sum and output
 // per head (base 2).  The RP row threads are merged through LDS at the end.
-template <int D, int HP, int SPL>
+template <int D, int HP, int SPL, bool NTV>
 __global__ __launch_bounds__(256)
 void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_new,
                         const bf16_t *__restrict__ v_new, bf16_t *__restrict__ k_cache,
@@ -146,8 +146,14 @@ void swska_decode_split(const bf16_t *__restrict__ q, const bf16_t *__restrict__
             if (jj < jend) {
                 kv[pp] = *reinterpret_cast<const uint4 *>(jj == jn ? kn : krow + (size_t)jj * D);
 #pragma unroll
-                for (int hh = 0; hh < HP; ++hh)
-                    vv[hh][pp] = *reinterpret_cast<const uint4 *>(jj == jn ? vn[hh] : vrow[hh] + (size_t)jj * D);
+                for (int hh = 0; hh < HP; ++hh) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(jj == jn ? vn[hh] : vrow[hh] + (size_t)jj * D);
+                    if constexpr (NTV)
+                        vv[hh][pp] = __builtin_bit_cast(
+                            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(src)));
+                    else
+                        vv[hh][pp] = *src;
+                }
             }
         }
         float sj[HP][G], mn[HP];
@@ -286,12 +292,29 @@ size_t swska_decode_blocks(int N, int H, int window) {
     return ((size_t)N * value_splits(window) + 7) / 8 * 8 * H;
 }
 
+// Value windows larger than this are read with streaming (non-temporal)
+// loads: they cannot stay in the 256 MB Infinity Cache from one step to the
+// next, and the hint keeps them from displacing the keys, which the other
+// heads' workgroups read again from L2.  Measured, 16 heads x 4096 slots x
+// 128: 64 sequences (1.07 GB of values) 198-202 -> 175-176 us per step; 32
+// sequences 107-109 -> 95 us; 16 sequences (268 MB) 47-50 against 50-51 us
+// with the hint, so smaller windows keep ordinary loads.
+constexpr size_t kValueStreamBytes = (size_t)384 << 20;
+
 template <int D, int HP, int SPL>
 static void launch_split(const SkaDecArgs &a, int S, float *part, hipStream_t st) {
     const size_t blocks = ((size_t)a.N * S + 7) / 8 * 8 * (a.H / HP);
-    hipLaunchKernelGGL((swska_decode_split<D, HP, SPL>), dim3((unsigned)blocks), dim3(256), 0, st, (const bf16_t *)a.q,
-                       (const bf16_t *)a.k_new, (const bf16_t *)a.v_new, (bf16_t *)a.k_cache, (bf16_t *)a.v_cache,
-                       a.pos, part, a.N, a.H, a.window, S, a.scale * kLog2e);
+    const bool ntv = (size_t)a.N * a.H * a.window * D * 2 > kValueStreamBytes;
+    if (ntv)
+        hipLaunchKernelGGL((swska_decode_split<D, HP, SPL, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const bf16_t *)a.q, (const bf16_t *)a.k_new, (const bf16_t *)a.v_new,
+                           (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H, a.window, S,
+                           a.scale * kLog2e);
+    else
+        hipLaunchKernelGGL((swska_decode_split<D, HP, SPL, false>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           (const bf16_t *)a.q, (const bf16_t *)a.k_new, (const bf16_t *)a.v_new,
+                           (bf16_t *)a.k_cache, (bf16_t *)a.v_cache, a.pos, part, a.N, a.H, a.window, S,
+                           a.scale * kLog2e);
 }
 
 // Splits of kSplitLong slots when that leaves at least 8 split workgroups per
