@@ -92,9 +92,10 @@ struct P {
 constexpr int kStS = 32;   // tokens per state step
 __global__ __launch_bounds__(256, 2)
 void bwd_state_kernel(P p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kD * kT32 * 2 + kD * 4];
+    __shared__ __attribute__((aligned(16))) char smem[2 * kD * kT32 * 2 + 2 * kD * 4];
     char *sX = smem, *sY = smem + kD * kT32 * 2;
-    float *sGam = reinterpret_cast<float *>(smem + 2 * kD * kT32 * 2);
+    // log2 decay of the current step per channel, and its power of two
+    float *sGam = reinterpret_cast<float *>(smem + 2 * kD * kT32 * 2), *sGamE = sGam + kD;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
     // the two roles of one (b,h, segment) are adjacent block ids, so that in a
     // packed batch both roles of the longest sequences are dispatched first
@@ -176,7 +177,10 @@ void bwd_state_kernel(P p) {
         for (int e = 0; e < 8; ++e) store_t_rows<2, kT32>(sX, 8 * cg + e, r, xT[e]);
         if (r == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sGam[8 * cg + e] = lend[e];
+            for (int e = 0; e < 8; ++e) {
+                sGam[8 * cg + e] = lend[e];
+                sGamE[8 * cg + e] = exp2_fast(lend[e]);
+            }
         }
         if (it + 1 < nst) load_raw<kStS, false>(R, rs, (rev ? stp - 1 : stp + 1) * kStS, r, cg);
         __syncthreads();
@@ -184,7 +188,7 @@ void bwd_state_kernel(P p) {
         // A (X^T layout): columns rr decay by 2^{Gam[rr]}; A += Y^T X
         const float gr = sGam[rr];
         dacc += gr;
-        const float er = exp2_fast(gr);
+        const float er = sGamE[rr];
         const bf16x8_t xB0 = lds16(sX, (rr * kT32 + 8 * h) * 2), xB1 = lds16(sX, (rr * kT32 + 16 + 8 * h) * 2);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -199,9 +203,9 @@ void bwd_state_kernel(P p) {
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
-                    const float4 gm = *reinterpret_cast<const float4 *>(sGam + 32 * q + 8 * a4 + 4 * h);
-                    B[q][4 * a4 + 0] *= exp2_fast(gm.x); B[q][4 * a4 + 1] *= exp2_fast(gm.y);
-                    B[q][4 * a4 + 2] *= exp2_fast(gm.z); B[q][4 * a4 + 3] *= exp2_fast(gm.w);
+                    const float4 gm = *reinterpret_cast<const float4 *>(sGamE + 32 * q + 8 * a4 + 4 * h);
+                    B[q][4 * a4 + 0] *= gm.x; B[q][4 * a4 + 1] *= gm.y;
+                    B[q][4 * a4 + 2] *= gm.z; B[q][4 * a4 + 3] *= gm.w;
                 }
                 B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 8 * h) * 2), yB0, B[q]);
                 B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 16 + 8 * h) * 2), yB1, B[q]);
