@@ -131,6 +131,106 @@ __device__ __forceinline__ void store_tile(char *buf, const uint4 (&rk)[Tile<D, 
     }
 }
 
+// S^T tile (64 keys x this wave's 32 queries) of the K tile staged at buf
+template <int D, int NT>
+__device__ __forceinline__ void qk_tile(const char *buf, const bf16x8_t (&qB)[D / 16], f32x16_t (&S)[2], int l32,
+                                        int h) {
+    using TL = Tile<D, NT>;
+    S[0] = f32x16_t{};
+    S[1] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(buf + ((32 * mt + l32) * TL::KROW + 16 * s + 8 * h) * 2);
+            S[mt] = mfma(a, qB[s], S[mt]);
+        }
+}
+
+// Online softmax of one S^T tile and O^T += V^T P^T with the V^T tile at buf.
+// With NEXT, the scores of the following tile (K tile at nbuf, into Sn) are
+// issued on the matrix cores inside the same straight-line blocks as the max
+// and the exponentials, so the two kinds of work overlap within the wave.
+template <int D, int NT, bool NEXT>
+__device__ __forceinline__ void softmax_pv(const char *buf, f32x16_t (&S)[2], f32x16_t (&O)[D / 32], float &m,
+                                           float &lsum, bool edge, int k0, int qi, int window, int T,
+                                           float scale_log2e, int l32, int h, const char *nbuf,
+                                           const bf16x8_t (&qB)[D / 16], f32x16_t (&Sn)[2]) {
+    using TL = Tile<D, NT>;
+    auto qk_part = [&](int s0, int s1) {
+#pragma unroll
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8_t a =
+                    *reinterpret_cast<const bf16x8_t *>(nbuf + ((32 * mt + l32) * TL::KROW + 16 * s + 8 * h) * 2);
+                Sn[mt] = mfma(a, qB[s], Sn[mt]);
+            }
+    };
+    if constexpr (NEXT) {
+        Sn[0] = f32x16_t{};
+        Sn[1] = f32x16_t{};
+    }
+    if (edge) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+                const bool ok = key <= qi && key > qi - window && key < T;
+                S[mt][i] = ok ? S[mt][i] : -INFINITY;
+            }
+    }
+    if constexpr (NEXT) qk_part(0, D / 32);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = mx * scale_log2e;   // scale > 0 keeps the order
+    const bool grow = mnew > m + kRescale;
+    if (__any(grow)) {
+        const float corr = grow ? exp2_fast(m - mnew) : 1.f;  // m = -inf -> 0
+        if (grow) m = mnew;
+        lsum *= corr;
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[mt][i] *= corr;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    if constexpr (NEXT) qk_part(D / 32, D / 16);
+    // P in bf16 (the MFMA operand); the row sum adds those same rounded values
+    // (v_dot2 against ones, two chains), so the normalised weights sum to one
+    // exactly as used
+    bf16x8_t P[4];
+    const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
+    float ls1 = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(S[s >> 1][8 * (s & 1) + e], scale_log2e, -mref));
+        uint4 u = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7]));
+        P[s] = __builtin_bit_cast(bf16x8_t, u);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.x), one2, lsum, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one2, ls1, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one2, lsum, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one2, ls1, false);
+    }
+    lsum += ls1;
+    // O^T += V^T P^T: k = key in the permuted order of the S^T accumulators
+    const char *vt = buf + TL::KBYTES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(vt + ((32 * mt + l32) * TL::VROW + 16 * s + 8 * h) * 2);
+            O[mt] = mfma(a, P[s], O[mt]);
+        }
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW)
 void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
@@ -138,7 +238,9 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                   int BH, int H, int T, int window, float scale_log2e, int nqb) {
     constexpr int NT = 64 * NW, kBQ = 32 * NW;
     using TL = Tile<D, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * TL::BYTES];
+    // three tile buffers: tile j is consumed (softmax, P V) while tile j+1's
+    // scores are computed from the next buffer and tile j+2 is written to the third
+    __shared__ __attribute__((aligned(16))) char smem[3 * TL::BYTES];
 
     // XCD-aware block -> (b*H + h, query block): XCD x = id % 8 walks the heads
     // x, x + 8, ... in increasing query-block order.
@@ -179,96 +281,52 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     float m = -INFINITY, lsum = 0.f;
 
     const int lo = max(0, q0 - window + 1);
-    const int hi = min(T, q0 + kBQ);        // exclusive
+    const int hi = min(T, q0 + kBQ);        // exclusive (> lo: q0 < T)
     const int kt0 = (lo / kBK) * kBK;
+    const int ntile = (hi - kt0 + kBK - 1) / kBK;
     // this wave's key range [wlo, whi]
     const int wlo = qw0 - window + 1, whi = qw0 + 31;
+    auto skip = [&](int k0) { return (k0 + kBK - 1 < wlo) || (k0 > whi); };
+    auto edge = [&](int k0) { return (k0 <= whi - window) || (k0 + kBK - 1 > qw0) || (k0 + kBK > T); };
 
     uint4 rk[TL::KVEC], rv[TL::KPT];
     fetch_tile<D, NT>(kr, vr, kt0, rk, rv);
     store_tile<D, NT>(smem, rk, rv);
+    if (ntile > 1) {
+        fetch_tile<D, NT>(kr, vr, kt0 + kBK, rk, rv);
+        store_tile<D, NT>(smem + TL::BYTES, rk, rv);
+    }
     __syncthreads();
+    if (ntile > 2) fetch_tile<D, NT>(kr, vr, kt0 + 2 * kBK, rk, rv);
 
-    int buf = 0;
-    for (int k0 = kt0; k0 < hi; k0 += kBK, buf ^= 1) {
-        const bool more = k0 + kBK < hi;
-        if (more) fetch_tile<D, NT>(kr, vr, k0 + kBK, rk, rv);
-        const char *cur = smem + buf * TL::BYTES;
-
-        const bool skip = (k0 + kBK - 1 < wlo) || (k0 > whi);
-        if (!skip) {
-            const bool edge = (k0 <= whi - window) || (k0 + kBK - 1 > qw0) || (k0 + kBK > T);
-            // S^T tile: 64 keys x 32 queries
-            f32x16_t S[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                        cur + ((32 * mt + l32) * TL::KROW + 16 * s + 8 * h) * 2);
-                    S[mt] = mfma(a, qB[s], S[mt]);
-                }
-            if (edge) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-                        const bool ok = key <= qi && key > qi - window && key < T;
-                        S[mt][i] = ok ? S[mt][i] : -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[mt][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = mx * scale_log2e;   // scale > 0 keeps the order
-            const bool grow = mnew > m + kRescale;
-            if (__any(grow)) {
-                const float corr = grow ? exp2_fast(m - mnew) : 1.f;  // m = -inf -> 0
-                if (grow) m = mnew;
-                lsum *= corr;
-#pragma unroll
-                for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) O[mt][i] *= corr;
-            }
-            const float mref = (m == -INFINITY) ? 0.f : m;
-            // P in bf16 (the MFMA operand); the row sum adds those same rounded
-            // values (v_dot2 against ones, two chains), so the normalised weights
-            // sum to one exactly as used
-            bf16x8_t P[4];
-            const bf16x2_t one2 = {(__bf16)1.f, (__bf16)1.f};
-            float ls1 = 0.f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(S[s >> 1][8 * (s & 1) + e], scale_log2e, -mref));
-                uint4 u = make_uint4(pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]),
-                                     pack2(p[6], p[7]));
-                P[s] = __builtin_bit_cast(bf16x8_t, u);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.x), one2, lsum, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one2, ls1, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one2, lsum, false);
-                ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one2, ls1, false);
-            }
-            lsum += ls1;
-            // O^T += V^T P^T: k = key in the permuted order of the S^T accumulators
-            const char *vt = cur + TL::KBYTES;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int mt = 0; mt < D / 32; ++mt) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                        vt + ((32 * mt + l32) * TL::VROW + 16 * s + 8 * h) * 2);
-                    O[mt] = mfma(a, P[s], O[mt]);
-                }
+    // One step: scores of tile j+1 (into Sn) beside the softmax and P V of
+    // tile j (from Sc), then tile j+2 to its buffer and tile j+3 in flight.
+    auto step = [&](int j, int bj, f32x16_t (&Sc)[2], f32x16_t (&Sn)[2]) {
+        const int k0 = kt0 + j * kBK;
+        const int b1 = bj == 2 ? 0 : bj + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+        const bool next = j + 1 < ntile && !skip(k0 + kBK);
+        const char *cur = smem + bj * TL::BYTES, *nb = smem + b1 * TL::BYTES;
+        if (!skip(k0)) {
+            if (next)
+                softmax_pv<D, NT, true>(cur, Sc, O, m, lsum, edge(k0), k0, qi, window, T, scale_log2e, l32, h, nb,
+                                        qB, Sn);
+            else
+                softmax_pv<D, NT, false>(cur, Sc, O, m, lsum, edge(k0), k0, qi, window, T, scale_log2e, l32, h, nb,
+                                         qB, Sn);
+        } else if (next) {
+            qk_tile<D, NT>(nb, qB, Sn, l32, h);
         }
-        if (more) store_tile<D, NT>(smem + (buf ^ 1) * TL::BYTES, rk, rv);
+        if (j + 2 < ntile) store_tile<D, NT>(smem + b2 * TL::BYTES, rk, rv);
         __syncthreads();
+        if (j + 3 < ntile) fetch_tile<D, NT>(kr, vr, k0 + 3 * kBK, rk, rv);
+        return b1;
+    };
+    f32x16_t Sa[2], Sb[2];
+    if (!skip(kt0)) qk_tile<D, NT>(smem, qB, Sa, l32, h);
+    int bj = 0;
+    for (int j = 0; j < ntile; j += 2) {
+        bj = step(j, bj, Sa, Sb);
+        if (j + 1 < ntile) bj = step(j + 1, bj, Sb, Sa);
     }
 
     const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -286,7 +344,6 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             }
     }
 }
-
 }  // namespace
 
 // The key and value descriptors address T rows of dk bf16 with 32-bit byte
