@@ -9,9 +9,10 @@
 //
 // Kernel: one workgroup = 32 NW consecutive queries of one (b, h); NW waves,
 // 32 queries each (NW = 8 at d = 128, one workgroup per CU; NW = 4 at d = 64,
-// two per CU).  Keys/values stream through LDS in tiles of 64 (double
-// buffered; the next tile is fetched into registers while the current one is
-// used), so each staged tile serves 32 NW queries.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
+// two per CU).  Keys/values stream through LDS in tiles of 64, three buffers
+// deep: while tile j is consumed, tile j+1's scores are computed and tile j+2
+// is written from registers (tile j+3 in flight), so each staged tile serves
+// 32 NW queries.  Per tile and wave, on v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T       keys on the M dimension, queries on lanes, so each lane
 //                     owns one query's scores and the softmax reductions stay
 //                     inside the lane (plus one exchange with lane^32);
@@ -21,6 +22,9 @@
 //   O^T += V^T P^T    P^T taken straight from the S^T accumulators (bf16) with a
 //                     permuted k order; V^T is stored in LDS in that key order,
 //                     so each operand is one 16-byte read.
+// The next tile's S^T products are issued inside the same straight-line code
+// as this tile's max and exponentials, so that matrix and vector instructions
+// of one wave overlap.
 // Tiles entirely outside a wave's window are skipped; tiles on the window's two
 // edges are masked element by element.  Workgroups are mapped so that each XCD
 // works on a fixed pair of heads in increasing query order, which keeps the
