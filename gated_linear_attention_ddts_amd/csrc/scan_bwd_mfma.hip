@@ -23,27 +23,25 @@
 //
 // Kernels:
 //   bwd_state_kernel    the state (forward order) and its gradient (reverse
-//                       order) per segment of 64-token chunks, on matrix cores;
-//                       writes a bf16 checkpoint of each at every 64 tokens:
-//                       S entering the chunk, and G leaving it in both
-//                       orientations, all in fragment order (frag_index), so
-//                       that the gradient kernel loads them as ready operands.
-//                       Segments start from zero (the first from S0, the last
-//                       from dS_T); each writes its fp32 edge state and total
-//                       decay.
+//                       order) per segment of 32-token chunks, on matrix cores;
+//                       writes a bf16 checkpoint of each at every chunk: S
+//                       entering the chunk and G leaving it, in fragment order
+//                       (frag_index), so that the gradient kernel loads them as
+//                       ready operands.  Segments start from zero (the first
+//                       from S0, the last from dS_T); each writes its fp32 edge
+//                       state and total decay.
 //   bwd_combine_kernel  (several segments only) runs the segment edges across
 //                       the sequence: the true state entering and gradient
 //                       leaving each segment (fragment order, bf16), and dS0.
 //                       A checkpoint c of segment s is completed on load as
 //                       S_c = S_loc_c + diag(2^{D_c}) S_in(s).
-//   bwd_grad_kernel     one workgroup per 32-token half of a checkpoint
-//                       interval; the half that does not start at a checkpoint
-//                       bridges to it through the other half (S through the
-//                       first half, G back through the second), then runs all
-//                       products above on the matrix cores and the element-wise
-//                       epilogue in the producer-lane layout.  Two workgroups
-//                       per CU; the two halves of an interval run on one XCD.
-//   bwd_fallback_kernel the listed wide-span halves, with the exact routine.
+//   bwd_grad_kernel     one workgroup per 32-token chunk: the two checkpoints
+//                       (G's transposed operands through LDS: an identity
+//                       product per 32x32 block turns its rows into columns),
+//                       all products above on the matrix cores and the
+//                       element-wise epilogue in the producer-lane layout.  Two
+//                       workgroups per CU.
+//   bwd_fallback_kernel the listed wide-span chunks, with the exact routine.
 #include <algorithm>
 
 #include "launch.h"
@@ -54,7 +52,7 @@ namespace rodimus {
 
 namespace {
 
-constexpr int kCk = 64;              // tokens per checkpoint interval
+constexpr int kCk = 32;              // tokens per checkpoint (one gradient workgroup)
 constexpr int kSub = 32;             // tokens per gradient workgroup
 constexpr int kFrag = 32 * 64 * 8;   // bf16 per 128x128 matrix in fragment order (32 KiB)
 constexpr int kT32 = 32 + 8;         // bf16 per transposed LDS row of 32 tokens (+16 B)
@@ -68,12 +66,12 @@ struct P {
     const bf16_t *q, *k, *v, *g, *th, *dO;
     const float *S0, *dST;
     float *dq, *dk, *dv, *dg, *dth, *dS0;
-    bf16_t *ckS, *ckG, *ckGT;     // [BH][nck] checkpoints, fragment order
+    bf16_t *ckS, *ckG;            // [BH][nck] checkpoints, fragment order
     float *sigS, *sigG;           // [BH][nck][128] 2^{log2 decay to / from the segment edge}
     float *segS, *segG;           // [BH][nseg][128][128] fp32 segment edge states (row-major)
     float *segDS, *segDG;         // [BH][nseg][128] total log2 decay of each segment
-    bf16_t *fixS, *fixG, *fixGT;  // [BH][nseg] incoming state / outgoing gradient, fragment order
-    int *bad;                     // [0] = count, then entries bh * (2 nck) + half index
+    bf16_t *fixS, *fixG;          // [BH][nseg] incoming state / outgoing gradient, fragment order
+    int *bad;                     // [0] = count, then entries bh * nck + chunk
     float *slot;                  // [kSlowWG][2][128][128] fallback scratch
     int BH, T, nck, nseg, seg_ck;
     // packed variable-length batch (seq_rows): sequence s = bh / H in rows
@@ -85,10 +83,8 @@ struct P {
 
 // ------------------------------------------------------------ state passes
 // Role 0: S (forward over the segment); role 1: G (reverse), in 32-token steps
-// with a checkpoint at every 64-token boundary.  Wave w keeps the transposed
-// 128 x 32 slice X^T[n][32w..32w+31] (rows n = value channel) in
-// accumulators; role 1 also keeps G[r][32w..32w+31] (rows r = key channel) for
-// the second orientation of the checkpoint.
+// with a checkpoint at every step.  Wave w keeps the transposed 128 x 32 slice
+// X^T[n][32w..32w+31] (rows n = value channel) in accumulators.
 constexpr int kStS = 32;   // tokens per state step
 __global__ __launch_bounds__(256, 2)
 void bwd_state_kernel(P p) {
@@ -120,7 +116,7 @@ void bwd_state_kernel(P p) {
     rs.th = rsrc(p.th + rowbase * kD, len);
     rs.q = rs.k;
 
-    f32x16_t A[4], B[4];
+    f32x16_t A[4];
     const float *init = rev ? (seg == p.nseg - 1 && p.dST ? p.dST + (size_t)bh * kD * kD : nullptr)
                             : (seg == 0 && p.S0 ? p.S0 + (size_t)bh * kD * kD : nullptr);
 #pragma unroll
@@ -131,32 +127,23 @@ void bwd_state_kernel(P p) {
             if (init) x = *reinterpret_cast<const float4 *>(init + rr * kD + 32 * q + 8 * a4 + 4 * h);
             A[q][4 * a4 + 0] = x.x; A[q][4 * a4 + 1] = x.y; A[q][4 * a4 + 2] = x.z; A[q][4 * a4 + 3] = x.w;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            B[q][i] = (rev && init) ? init[(32 * q + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + rr] : 0.f;
     }
     float dacc = 0.f;  // log2 decay between the segment edge and the current step, channel rr
 
     Raw<kStS, false> R;
-    const int nst = 2 * (c_hi - c_lo);
-    const int st_first = rev ? 2 * c_hi - 1 : 2 * c_lo;
+    const int nst = c_hi - c_lo;
+    const int st_first = rev ? c_hi - 1 : c_lo;
     if (nst > 0) load_raw<kStS, false>(R, rs, st_first * kStS, r, cg);
     for (int it = 0; it < nst; ++it) {
         const int stp = rev ? st_first - it : st_first + it;
         const int t0 = stp * kStS;
-        if ((stp & 1) == (rev ? 1 : 0)) {
-            // checkpoint: S entering chunk c (role 0) / G leaving it (role 1)
-            const size_t ck = (size_t)bh * p.nck + (stp >> 1);
+        {
+            // checkpoint: S entering chunk stp (role 0) / G leaving it (role 1)
+            const size_t ck = (size_t)bh * p.nck + stp;
             bf16_t *dA = (rev ? p.ckG : p.ckS) + ck * kFrag;
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 st_stream(reinterpret_cast<bf16x8_t *>(dA + ((8 * w + s) * 64 + l) * 8), cvt8(A[s >> 1], 8 * (s & 1)));
-            if (rev) {
-                bf16_t *dB = p.ckGT + ck * kFrag;
-#pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    st_stream(reinterpret_cast<bf16x8_t *>(dB + ((8 * w + s) * 64 + l) * 8), cvt8(B[s >> 1], 8 * (s & 1)));
-            }
             if (h == 0) (rev ? p.sigG : p.sigS)[ck * kD + rr] = exp2_fast(dacc);
         }
 
@@ -196,21 +183,6 @@ void bwd_state_kernel(P p) {
             A[q] = mfma(lds16(sY, ((32 * q + l32) * kT32 + 8 * h) * 2), xB0, A[q]);
             A[q] = mfma(lds16(sY, ((32 * q + l32) * kT32 + 16 + 8 * h) * 2), xB1, A[q]);
         }
-        if (rev) {
-            // B (rows = key channel): rows decay; B += X^T Y
-            const bf16x8_t yB0 = lds16(sY, (rr * kT32 + 8 * h) * 2), yB1 = lds16(sY, (rr * kT32 + 16 + 8 * h) * 2);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const float4 gm = *reinterpret_cast<const float4 *>(sGamE + 32 * q + 8 * a4 + 4 * h);
-                    B[q][4 * a4 + 0] *= gm.x; B[q][4 * a4 + 1] *= gm.y;
-                    B[q][4 * a4 + 2] *= gm.z; B[q][4 * a4 + 3] *= gm.w;
-                }
-                B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 8 * h) * 2), yB0, B[q]);
-                B[q] = mfma(lds16(sX, ((32 * q + l32) * kT32 + 16 + 8 * h) * 2), yB1, B[q]);
-            }
-        }
         __syncthreads();
     }
 
@@ -242,7 +214,7 @@ void bwd_combine_kernel(P p) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)p.BH * kD * kD) return;
     const int bh = (int)(idx >> 14), e = (int)(idx & 16383), r = e >> 7, n = e & 127;
-    const int fi = frag_index(r, n), fiT = frag_index(n, r);
+    const int fi = frag_index(r, n);
     float S = 0.f;
     for (int s = 0; s < p.nseg; ++s) {
         const size_t sb = (size_t)bh * p.nseg + s;
@@ -252,10 +224,7 @@ void bwd_combine_kernel(P p) {
     float G = 0.f;
     for (int s = p.nseg - 1; s >= 0; --s) {
         const size_t sb = (size_t)bh * p.nseg + s;
-        if (s < p.nseg - 1) {
-            p.fixG[sb * kFrag + fi] = f2bf(G);
-            p.fixGT[sb * kFrag + fiT] = f2bf(G);
-        }
+        if (s < p.nseg - 1) p.fixG[sb * kFrag + fi] = f2bf(G);
         G = fmaf(exp2_fast(p.segDG[sb * kD + r]), G, p.segG[sb * kD * kD + e]);
     }
     if (p.dS0) p.dS0[idx] = G;
@@ -263,19 +232,17 @@ void bwd_combine_kernel(P p) {
 
 // ---------------------------------------------------------- gradient kernel
 // LDS (bytes).  Token rows [32][136] bf16 (channels permuted): Qt, Kh, Kb, dO,
-// V; transposed rows [128][40] bf16 (tokens permuted): Qt^T, Kh^T, dO^T; fp32
-// 2^Gam of the bridged half, the decay term, the sigma of the G^T fix-up.  The
-// bridge operands alias Qt^T / Kh^T (written after the bridge); the fp32
-// staging of the epilogue aliases all operand rows.
+// V; transposed rows [128][40] bf16 (tokens permuted): Qt^T, Kh^T, dO^T; the
+// fp32 decay term.  G's columns pass through the Qt^T / Kh^T area before those
+// are written; the fp32 staging of the epilogue aliases all operand rows.
 constexpr int kRowB = kSub * kQR * 2;           // 8704
 constexpr int kTB = kD * kT32 * 2;              // 10240
 constexpr int kOffQr = 0, kOffKr = kRowB, kOffKbr = 2 * kRowB, kOffDOr = 3 * kRowB, kOffVr = 4 * kRowB;
 constexpr int kOffQT = 5 * kRowB, kOffKT = kOffQT + kTB, kOffDOT = kOffKT + kTB;
-constexpr int kOffGamB = kOffDOT + kTB, kOffDec = kOffGamB + kD * 4;
-constexpr int kOffSig = kOffDec + kD * 4;
-constexpr int kGradLDS = kOffSig + kD * 4;
-constexpr int kOffB1 = kOffQT, kOffB2 = kOffKT;
-static_assert(4 * kSub * kSR * 4 <= kOffGamB, "staging fits in the dead operand rows");
+constexpr int kOffDec = kOffDOT + kTB;
+constexpr int kGradLDS = kOffDec + kD * 4;
+static_assert(4 * kSub * kSR * 4 <= kOffDec, "staging fits in the dead operand rows");
+static_assert(64 * kD * 2 <= 2 * kTB, "half of G's columns fit in the Qt^T / Kh^T area");
 static_assert(kGradLDS <= 80 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ bf16x8_t pack_frag(const float (&x)[8]) {
@@ -296,24 +263,34 @@ __device__ __forceinline__ uint4 fix_raw(const uint4 &x, const uint4 &y, float s
     return __builtin_bit_cast(uint4, pack_frag(a));
 }
 
-// One 32-token half (c, half) of checkpoint interval c; the other half of c is
-// the one bridged through.
+// Identity operands: fragment j of lane (l32, h) holds 1 where the column of
+// k-slot 8h + e of the j-th 16-column block equals l32.
+__device__ __forceinline__ void make_ident(bf16x8_t (&Id)[2], int l32, int h) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (16 * j + perm16(8 * h + e) == l32) ? 1.f : 0.f;
+        Id[j] = pack_frag(x);
+    }
+}
+// byte offset of 16-byte chunk ch (0..15) of column n (0..63 within a pass) of
+// G in the transposition area (XOR-swizzled by column: no bank conflicts, no
+// padding)
+__device__ __forceinline__ int gt_off(int n, int ch) { return kOffQT + n * (kD * 2) + ((ch ^ (n & 15)) << 4); }
+
+// One 32-token chunk c of one (b,h).
 __global__ __launch_bounds__(256, 2)
 void bwd_grad_kernel(P p) {
     __shared__ __attribute__((aligned(16))) char smem[kGradLDS];
-    float *sGamB = reinterpret_cast<float *>(smem + kOffGamB);
     float *sDec = reinterpret_cast<float *>(smem + kOffDec);
-    float *sSig = reinterpret_cast<float *>(smem + kOffSig);
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-    // block -> (interval, half); the two halves of an interval share blockIdx % 8 (one XCD)
-    const int pair = (int)(blockIdx.x >> 4) * 8 + (int)(blockIdx.x & 7);
-    const int half = (blockIdx.x >> 3) & 1;
-    if (pair >= p.BH * p.nck) return;
-    const int bh = uni(pair / p.nck), c = uni(pair % p.nck);
+    const int ckb = (int)blockIdx.x;
+    const int bh = uni(ckb / p.nck), c = uni(ckb % p.nck);
     size_t rowbase;
     int len;
     seq_rows(p.cu, p.H, p.total, p.T, bh, rowbase, len);
-    const int tc = c * kCk, t0 = tc + kSub * half;
+    const int t0 = c * kCk;
     if (t0 >= len) return;
     const int seg = c / p.seg_ck;
     const bool fixS = seg > 0, fixG = seg < p.nseg - 1;
@@ -325,26 +302,16 @@ void bwd_grad_kernel(P p) {
     const __amdgpu_buffer_rsrc_t rv = rsrc(p.v + rowbase * kD, len), rg = rsrc(p.g + rowbase * kD, len);
     const __amdgpu_buffer_rsrc_t rth = rsrc(p.th + rowbase * kD, len), rdo = rsrc(p.dO + rowbase * kD, len);
 
-    // this half's inputs, and the other half's for the bridge (tokens past the end read 0)
-    uint4 Rq[2], Rk[2], Rv[2], Rg[2], Rth[2], Rdo[2], Bx[2], By[2], Bg[2], Bth[2];
-    const int ts = half ? tc : tc + kSub;
+    // this chunk's inputs (tokens past the end read 0)
+    uint4 Rq[2], Rk[2], Rv[2], Rg[2], Rth[2], Rdo[2];
     load_one<2>(Rg, rg, t0, r, cg);
     load_one<2>(Rth, rth, t0, r, cg);
     load_one<2>(Rq, rq, t0, r, cg);
     load_one<2>(Rk, rk, t0, r, cg);
     load_one<2>(Rv, rv, t0, r, cg);
     load_one<2>(Rdo, rdo, t0, r, cg);
-    load_one<2>(Bg, rg, ts, r, cg);
-    load_one<2>(Bth, rth, ts, r, cg);
-    if (half) {
-        load_one<2>(Bx, rk, ts, r, cg);
-        load_one<2>(By, rv, ts, r, cg);
-    } else {
-        load_one<2>(Bx, rq, ts, r, cg);
-        load_one<2>(By, rdo, ts, r, cg);
-    }
 
-    // this half's gates; span check (Kh = k 2^{mu - Lam} must stay finite)
+    // this chunk's gates; span check (Kh = k 2^{mu - Lam} must stay finite)
     uint32_t qTp[8], kTp[8];  // Qt^T / Kh^T rows of this lane's 8 channels, 2 tokens packed
     {
         float l2a[2][8], l2b[2][8], lend[8];
@@ -355,7 +322,7 @@ void bwd_grad_kernel(P p) {
         if (__syncthreads_or(bad)) {
             if (tid == 0) {
                 const int i = atomicAdd(p.bad, 1);
-                p.bad[1 + i] = bh * (2 * p.nck) + 2 * c + half;
+                p.bad[1 + i] = (int)ck;
             }
             return;
         }
@@ -388,139 +355,64 @@ void bwd_grad_kernel(P p) {
             kTp[e] = pack2(kT[e][0], kT[e][1]);
         }
     }
-    // this interval's checkpoints, raw: all loads in flight at once, their
-    // latency overlapping the bridge operands
-    const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag, *cGT = p.ckGT + ck * kFrag;
-    uint4 rS[8], rG[8], rGT[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        rS[s] = ld_raw(cS, 8 * w + s, l);
-        rG[s] = ld_raw(cG, 8 * w + s, l);
-        rGT[s] = ld_raw(cGT, 8 * w + s, l);
-    }
-    // bridge operands: first half -> Kb0^T, V0^T (the state through it);
-    // second half -> Qt1^T, dO1^T (the gradient back through it)
+    // S entering and G leaving this chunk, bf16 operands: the checkpoints of
+    // later / earlier segments completed with the segment fix-up
+    bf16x8_t Sf[8], Gf[8], GTf[8];
     {
-        float l2a[2][8], l2b[2][8], lend[8];
-        gates_scan_gt<kSub>(Bg, Bth, ts, len, r, l, l2a, l2b, lend);
-        float xT[8][2];
+        const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag;
+        uint4 rS[8], rG[8], fS[8], fG[8];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            float xf[8];
-            unpack8(Bx[tt], xf);
+        for (int s = 0; s < 8; ++s) {
+            rS[s] = ld_raw(cS, 8 * w + s, l);
+            rG[s] = ld_raw(cG, 8 * w + s, l);
+        }
+        const float sigS = fixS ? p.sigS[ck * kD + rr] : 0.f;
+        const float sigG = fixG ? p.sigG[ck * kD + rr] : 0.f;
+        if (fixS) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                xT[e][tt] = xf[e] * exp2_fast(half ? l2b[tt][e] + lend[e] - l2a[tt][e] : l2a[tt][e]);
+            for (int s = 0; s < 8; ++s) fS[s] = ld_raw(p.fixS + sb * kFrag, 8 * w + s, l);
+        }
+        if (fixG) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) fG[s] = ld_raw(p.fixG + sb * kFrag, 8 * w + s, l);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) store_t_rows<2, kT32>(smem + kOffB1, 8 * cg + e, r, xT[e]);
-        store_vt<2, kT32>(smem + kOffB2, cg, r, By);
-        if (r == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sGamB[8 * cg + e] = exp2_fast(lend[e]);
+        for (int s = 0; s < 8; ++s) {
+            Sf[s] = __builtin_bit_cast(bf16x8_t, fixS ? fix_raw(rS[s], fS[s], sigS) : rS[s]);
+            Gf[s] = __builtin_bit_cast(bf16x8_t, fixG ? fix_raw(rG[s], fG[s], sigG) : rG[s]);
         }
     }
-    if (fixG && tid < kD) sSig[tid] = p.sigG[ck * kD + tid];
-    __syncthreads();
+    // G's columns (G^T operands) through LDS, in two passes of 64 columns over
+    // the Qt^T / Kh^T area (written only after the first product): each wave
+    // turns its 32 rows into columns by an identity product per 32x32 block,
+    // leaving column 32t + l32 of its rows (fragments 2w, 2w+1 of that column's
+    // operand) in lane l32 of block t.
+    {
+        bf16x8_t Id[2];
+        make_ident(Id, l32, h);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            __syncthreads();  // pass 0: operand rows written; pass 1: pass 0 read
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int t = 2 * pass + tb;
+                f32x16_t cc = {};
+                cc = mfma(Gf[2 * t], Id[0], cc);
+                cc = mfma(Gf[2 * t + 1], Id[1], cc);
+                const int n = 32 * tb + l32;
+                *reinterpret_cast<bf16x8_t *>(smem + gt_off(n, 2 * (2 * w) + h)) = cvt8(cc, 0);
+                *reinterpret_cast<bf16x8_t *>(smem + gt_off(n, 2 * (2 * w + 1) + h)) = cvt8(cc, 8);
+            }
+            __syncthreads();
+            if ((w >> 1) == pass) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) GTf[s] = lds16(smem, gt_off(rr - 64 * pass, 2 * s + h));
+            }
+        }
+    }
 
     auto rowf = [&](int off, int row, int s) { return lds16(smem, off + (row * kQR + 16 * s + 8 * h) * 2); };
     auto trf = [&](int off, int row, int ks) { return lds16(smem, off + (row * kT32 + 16 * ks + 8 * h) * 2); };
-
-    // S entering and G (both orientations) leaving this half, bf16 operands;
-    // checkpoints of later / earlier segments are completed with the segment
-    // fix-up (loaded all at once)
-    bf16x8_t Sf[8], Gf[8], GTf[8];
-    const float sigS = fixS ? p.sigS[ck * kD + rr] : 0.f;
-    const float sigG = fixG ? sSig[rr] : 0.f;
-    const bf16_t *xS = p.fixS + sb * kFrag, *xG = p.fixG + sb * kFrag, *xGT = p.fixGT + sb * kFrag;
-    if (fixS) {
-        uint4 f[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) f[s] = ld_raw(xS, 8 * w + s, l);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) rS[s] = fix_raw(rS[s], f[s], sigS);
-    }
-    if (fixG) {
-        uint4 f[8], fT[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            f[s] = ld_raw(xG, 8 * w + s, l);
-            fT[s] = ld_raw(xGT, 8 * w + s, l);
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            rG[s] = fix_raw(rG[s], f[s], sigG);
-            float x[8], y[8];
-            unpack8(rGT[s], x);
-            unpack8(fT[s], y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = fmaf(sSig[16 * s + 8 * (e >> 2) + 4 * h + (e & 3)], y[e], x[e]);
-            rGT[s] = __builtin_bit_cast(uint4, pack_frag(x));
-        }
-    }
-    if (half) {
-        // S through the first half: diag(2^{Gam0}) S_c + Kb0^T V0 (transposed accumulators)
-        const float eg = sGamB[rr];
-        f32x16_t A[4];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            float x[8];
-            unpack8(rS[s], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) A[q] = mfma(trf(kOffB2, 32 * q + l32, ks), trf(kOffB1, rr, ks), A[q]);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            Sf[s] = cvt8(A[s >> 1], 8 * (s & 1));
-            Gf[s] = __builtin_bit_cast(bf16x8_t, rG[s]);
-            GTf[s] = __builtin_bit_cast(bf16x8_t, rGT[s]);
-        }
-    } else {
-        // G back through the second half: diag(2^{Gam1}) G_c + Qt1^T dO1, both
-        // orientations, one after the other
-        {
-            f32x16_t A[4];
-            const float eg = sGamB[rr];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                float x[8];
-                unpack8(rG[s], x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) A[s >> 1][8 * (s & 1) + e] = x[e] * eg;
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) A[q] = mfma(trf(kOffB2, 32 * q + l32, ks), trf(kOffB1, rr, ks), A[q]);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Gf[s] = cvt8(A[s >> 1], 8 * (s & 1));
-        }
-        {
-            f32x16_t B[4];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                float x[8];
-                unpack8(rGT[s], x);
-                const float4 g0 = *reinterpret_cast<const float4 *>(sGamB + 16 * s + 4 * h);
-                const float4 g1 = *reinterpret_cast<const float4 *>(sGamB + 16 * s + 8 + 4 * h);
-                const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) B[s >> 1][8 * (s & 1) + e] = x[e] * gm[e];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) B[q] = mfma(trf(kOffB1, 32 * q + l32, ks), trf(kOffB2, rr, ks), B[q]);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) GTf[s] = cvt8(B[s >> 1], 8 * (s & 1));
-        }
-#pragma unroll
-        for (int s = 0; s < 8; ++s) Sf[s] = __builtin_bit_cast(bf16x8_t, rS[s]);
-    }
 
     // ---- matrix-core products (wave w: output columns 32w..32w+31) ----
     // dv = A^T dO + Kb G (rows j, column rr), straight to memory
@@ -543,7 +435,7 @@ void bwd_grad_kernel(P p) {
             if (t0 + j < len) st_stream(&p.dv[(rowbase + t0 + j) * kD + rr], av[i]);
         }
     }
-    __syncthreads();  // bridge operands are dead: Qt^T, Kh^T take their place
+    __syncthreads();  // G's columns are read: Qt^T, Kh^T take their place
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         *reinterpret_cast<uint32_t *>(smem + kOffQT + ((8 * cg + e) * kT32 + perm16(2 * r)) * 2) = qTp[e];
@@ -700,45 +592,23 @@ void bwd_grad_kernel(P p) {
 }
 
 // --------------------------------------------------------------- fallback
-// Listed halves, exactly: rebuild S entering and G leaving the half in fp32
-// (row-major, this workgroup's scratch slot), then the pairwise routine.
+// Listed chunks, exactly: S entering and G leaving the chunk (its checkpoints
+// with the segment fix-ups) in fp32 (row-major, this workgroup's scratch slot),
+// then the pairwise routine.
 __global__ __launch_bounds__(256)
 void bwd_fallback_kernel(P p) {
     __shared__ float smem[kBodyFloats];
     const int n_bad = p.bad[0];
     const int tid = threadIdx.x;
     float *Ss = p.slot + (size_t)blockIdx.x * 2 * kD * kD, *Gs = Ss + kD * kD;
-    const int nsub = 2 * p.nck;
     for (int i = blockIdx.x; i < n_bad; i += gridDim.x) {
         const int ent = p.bad[1 + i];
-        const int bh = ent / nsub, sub = ent % nsub, c = sub >> 1, half = sub & 1;
+        const int bh = ent / p.nck, c = ent % p.nck;
         const int seg = c / p.seg_ck;
-        const size_t ck = (size_t)bh * p.nck + c, sb = (size_t)bh * p.nseg + seg;
+        const size_t ck = (size_t)ent, sb = (size_t)bh * p.nseg + seg;
         size_t rowbase;
         int len;
         seq_rows(p.cu, p.H, p.total, p.T, bh, rowbase, len);
-        const size_t xbase = rowbase * kD;
-        const int ts = c * kCk + (half ? 0 : kSub);  // the other half of the interval
-        const int Ls = min(kSub, len - ts);
-        float *lam = smem, *mu = lam + kBC * kBD, *X = mu + kBC * kBD, *Y = X + kBC * kBD;
-        chunk_gates<bf16_t>(p.g, p.th, xbase, ts, Ls, kD, lam, mu);
-        for (int e = tid; e < kSub * kD; e += 256) {
-            const int t = e >> 7, rc = e & 127;
-            float x = 0.f, y = 0.f;
-            if (t < Ls) {
-                const size_t xi = xbase + (size_t)(ts + t) * kD + rc;
-                if (half) {
-                    x = bf2f(p.k[xi]) * __expf(lam[(kBC - 1) * kBD + rc] - lam[t * kBD + rc] + mu[t * kBD + rc]);
-                    y = bf2f(p.v[xi]);
-                } else {
-                    x = bf2f(p.q[xi]) * __expf(lam[t * kBD + rc]);
-                    y = bf2f(p.dO[xi]);
-                }
-            }
-            X[e] = x;
-            Y[e] = y;
-        }
-        __syncthreads();
         const int n = tid & 127;
         for (int rr = tid >> 7; rr < kD; rr += 2) {
             const int fi = frag_index(rr, n);
@@ -746,17 +616,12 @@ void bwd_fallback_kernel(P p) {
             if (seg > 0) s = fmaf(p.sigS[ck * kD + rr], bf2f(p.fixS[sb * kFrag + fi]), s);
             float gg = bf2f(p.ckG[ck * kFrag + fi]);
             if (seg < p.nseg - 1) gg = fmaf(p.sigG[ck * kD + rr], bf2f(p.fixG[sb * kFrag + fi]), gg);
-            float acc = 0.f;
-            for (int t = 0; t < Ls; ++t) acc = fmaf(X[t * kD + rr], Y[t * kD + n], acc);
-            const float d = __expf(lam[(kBC - 1) * kBD + rr]);
-            if (half) s = fmaf(d, s, acc);
-            else gg = fmaf(d, gg, acc);
             Ss[rr * kD + n] = s;
             Gs[rr * kD + n] = gg;
         }
         __syncthreads();
         chunk_grads_body<bf16_t>(p.q, p.k, p.v, p.g, p.th, p.dO, Ss, Gs, p.dq, p.dk, p.dv, p.dg, p.dth, rowbase,
-                                 len, kD, kD, sub, smem);
+                                 len, kD, kD, c, smem);
         __syncthreads();
     }
 }
@@ -764,8 +629,7 @@ void bwd_fallback_kernel(P p) {
 // --------------------------------------------------------------- planning
 struct Plan {
     int nck, nseg, seg_ck;
-    size_t o_ckS, o_ckG, o_ckGT, o_sigS, o_sigG, o_segS, o_segG, o_segDS, o_segDG, o_fixS, o_fixG, o_fixGT,
-        o_bad, o_slot, bytes;
+    size_t o_ckS, o_ckG, o_sigS, o_sigG, o_segS, o_segG, o_segDS, o_segDG, o_fixS, o_fixG, o_bad, o_slot, bytes;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -783,7 +647,6 @@ Plan plan(long long BH, int T) {
     size_t o = 0;
     q.o_ckS = o; o += up256(nck * F);
     q.o_ckG = o; o += up256(nck * F);
-    q.o_ckGT = o; o += up256(nck * F);
     q.o_sigS = o; o += up256(nck * kD * 4);
     q.o_sigG = o; o += up256(nck * kD * 4);
     q.o_segS = o; o += up256(nsg * kD * kD * 4);
@@ -792,8 +655,7 @@ Plan plan(long long BH, int T) {
     q.o_segDG = o; o += up256(nsg * kD * 4);
     q.o_fixS = o; o += up256(nsg * F);
     q.o_fixG = o; o += up256(nsg * F);
-    q.o_fixGT = o; o += up256(nsg * F);
-    q.o_bad = o; o += up256((1 + 2 * nck) * 4);
+    q.o_bad = o; o += up256((1 + nck) * 4);
     q.o_slot = o; o += (size_t)kSlowWG * 2 * kD * kD * 4;
     q.bytes = o;
     return q;
@@ -815,7 +677,7 @@ uint64_t scan_bwd_mfma_launch_items(long long BH, int T) {
     const Plan q = plan(BH, T);
     uint64_t m = (uint64_t)2 * BH * q.nseg * 256;                               // state passes
     if (q.nseg > 1) m = std::max<uint64_t>(m, (uint64_t)BH * kD * kD);          // combine
-    m = std::max<uint64_t>(m, ((uint64_t)BH * q.nck + 7) / 8 * 16 * 256);       // gradients
+    m = std::max<uint64_t>(m, (uint64_t)BH * q.nck * 256);                      // gradients
     return std::max<uint64_t>(m, (uint64_t)kSlowWG * 256);                      // fallback
 }
 
@@ -828,11 +690,11 @@ void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
     p.g = (const bf16_t *)a.g; p.th = (const bf16_t *)a.tau; p.dO = (const bf16_t *)a.dO;
     p.S0 = a.S0; p.dST = a.dS_T;
     p.dq = a.dq; p.dk = a.dk_; p.dv = a.dv_; p.dg = a.dg; p.dth = a.dtau; p.dS0 = a.dS0;
-    p.ckS = (bf16_t *)(ws + q.o_ckS); p.ckG = (bf16_t *)(ws + q.o_ckG); p.ckGT = (bf16_t *)(ws + q.o_ckGT);
+    p.ckS = (bf16_t *)(ws + q.o_ckS); p.ckG = (bf16_t *)(ws + q.o_ckG);
     p.sigS = (float *)(ws + q.o_sigS); p.sigG = (float *)(ws + q.o_sigG);
     p.segS = (float *)(ws + q.o_segS); p.segG = (float *)(ws + q.o_segG);
     p.segDS = (float *)(ws + q.o_segDS); p.segDG = (float *)(ws + q.o_segDG);
-    p.fixS = (bf16_t *)(ws + q.o_fixS); p.fixG = (bf16_t *)(ws + q.o_fixG); p.fixGT = (bf16_t *)(ws + q.o_fixGT);
+    p.fixS = (bf16_t *)(ws + q.o_fixS); p.fixG = (bf16_t *)(ws + q.o_fixG);
     p.bad = (int *)(ws + q.o_bad);
     p.slot = (float *)(ws + q.o_slot);
     p.BH = BH; p.T = a.T; p.nck = q.nck; p.nseg = q.nseg; p.seg_ck = q.seg_ck;
@@ -843,8 +705,7 @@ void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
         const size_t n = (size_t)BH * kD * kD;
         hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
     }
-    const size_t npair = (size_t)BH * q.nck;
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)((npair + 7) / 8 * 16)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)((size_t)BH * q.nck)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(bwd_fallback_kernel, dim3(kSlowWG), dim3(256), 0, st, p);
 }
 

@@ -248,13 +248,13 @@ int rodimus_scan_prefill_varlen(const void *q, const void *k, const void *v, con
  * (256 threads per 32-token chunk); beyond that RODIMUS_ERR_INVALID_ARG.
  * Two paths, chosen from the arguments:
  *   - bf16 with dk = dv = 128: matrix cores (bf16 operands, fp32
- *     accumulation, bf16 state checkpoints every 64 tokens); same accuracy
- *     class as the bf16 forward;
+ *     accumulation, bf16 checkpoints of the state and its gradient every 32
+ *     tokens); same accuracy class as the bf16 forward;
  *   - otherwise: fp32 vector arithmetic over 32-token chunks with fp32
  *     checkpoints (workspace 2*B*H*ceil(T/32)*dk*dv fp32).
  * `workspace` must hold rodimus_scan_backward_workspace_bytes(...) bytes, else
  * RODIMUS_ERR_INVALID_ARG; its contents are overwritten (on the matrix-core
- * path: about 96 KiB per (b,h) per 64 tokens, plus per-segment edges and a
+ * path: about 65 KiB per (b,h) per 32 tokens, plus per-segment edges and a
  * fixed 32 MiB).  T = 0 copies dS_T (or zeros) into grad_S0.  Calls that
  * share one workspace must not overlap.
  */

@@ -188,16 +188,16 @@ def test_scan_backward_rejects(kw):
 
 def _mfma_bwd_workspace(B, H, T):
     """Workspace of the matrix-core backward (bf16, dk = dv = 128): bf16
-    checkpoints every 64 tokens (S, G, G^T: 32 KiB each), per-checkpoint decay
+    checkpoints of S and G every 32 tokens (32 KiB each), per-checkpoint decay
     factors, per-segment edges, the fallback list and 256 scratch pairs."""
     up = lambda x: (x + 255) // 256 * 256
     BH = B * H
-    nck = -(-T // 64)
+    nck = -(-T // 32)
     nseg = max(1, min(nck, -(-256 // BH)))
     seg_ck = -(-nck // nseg)
     nseg = -(-nck // seg_ck)
-    return (3 * up(BH * nck * 32768) + 2 * up(BH * nck * 512) + 2 * up(BH * nseg * 65536)
-            + 2 * up(BH * nseg * 512) + 3 * up(BH * nseg * 32768) + up(4 * (1 + 2 * BH * nck))
+    return (2 * up(BH * nck * 32768) + 2 * up(BH * nck * 512) + 2 * up(BH * nseg * 65536)
+            + 2 * up(BH * nseg * 512) + 2 * up(BH * nseg * 32768) + up(4 * (1 + BH * nck))
             + 256 * 2 * 128 * 128 * 4)
 
 
