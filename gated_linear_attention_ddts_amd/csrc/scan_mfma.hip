@@ -26,8 +26,15 @@
 //            decay of the later chunks folds into the operand exponent:
 //            S_loc = sum_c (Kb_c * 2^{rho_c})^T V_c, rho_c = sum of Lam_end after c;
 //            there is no state rescaling and nothing can overflow;
-//   phase 2 (scan_combine_kernel): S_in of every segment, left to right;
+//   phase 2: S_in of every segment, left to right: folded by the output
+//            pass's consumer waves from the sub-segment states before their
+//            first chunk when a segment has at most kFoldMax of them before
+//            it, else by scan_combine_kernel;
 //   phase 3 (scan_full_kernel): every segment from its S_in, writing o.
+// The sub-segment states are stored lane-major: float4 k (0..15) of lane
+// (wave w, lane l) of a 4-wave MFMA layout at [k][64 w + l], i.e. the 4
+// accumulator registers 4k..4k+3 of the lane that owns them in both kernels,
+// so each lane reads its 64 values as 16 coalesced 16-byte loads.
 //
 // scan_full_kernel: 8 waves.  Waves 0-3 (producers) turn chunk k's raw inputs
 // into LDS operands (gates, DPP scan of log2 a inside 16-lane rows, Qt, Kh,
@@ -59,6 +66,7 @@ namespace rodimus {
 namespace {
 
 constexpr int kCUs = 256;
+constexpr int kFoldMax = 8;        // sub-segment states a consumer wave folds itself
 constexpr int kMaxT = 1 << 23;     // 32-bit buffer offsets (T * 256 bytes)
 
 // LDS buffer layout (bytes); rows padded by 16 bytes (conflict-free 16-byte reads)
@@ -78,9 +86,10 @@ struct Params {
     const float *S0;  // [BH][128][128] or null (zeros)
     bf16_t *o;
     float *S_T;       // [BH][128][128] or null
-    float *wsS;       // [(G-1)*P][BH][128][128] sub-segment states / incoming states
-    float *wsA;       // [(G-1)*P][BH][128] total log2 decay of each sub-segment
+    float *wsS;       // [(G-1)*P][BH][16][256] float4: sub-segment states (lane-major) / incoming states
+    float *wsA;       // [(G-1)*P][BH][128] total decay of each sub-segment (a power of two)
     int BH, T, G, seg_len, P, sub_len;
+    int fold;         // the output pass folds the sub-segment states itself (no combine)
     // packed variable-length batch: sequence s = bh / H occupies rows
     // cu[s] .. cu[s+1]-1 of head h = bh % H's [total][128] rows; T is then the
     // longest length (the segment plan)
@@ -254,14 +263,44 @@ void scan_full_kernel(Params p) {
     int cbar_target = 0;
     const int n = 32 * cw + l32;
     f32x16_t S[4];                        // rows 32mt + 8a + 4h + r4, column n
-    {
-        const float *Sin = (seg == 0) ? (p.S0 ? p.S0 + (size_t)bh * kD * kD : nullptr)
-                                      : p.wsS + ((size_t)(seg * p.P - 1) * p.BH + bh) * kD * kD;
+    if (seg == 0 || p.fold) {
+        // S0 (row-major), then, for a later segment, every earlier sub-segment
+        // state folded in: S <- diag(2^{A_j}) S + S_j
+        const float *S0 = p.S0 ? p.S0 + (size_t)bh * kD * kD : nullptr;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                S[mt][i] = Sin ? Sin[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + n] : 0.f;
+                S[mt][i] = S0 ? S0[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + n] : 0.f;
+        const int nj = seg * p.P;
+        for (int j = 0; j < nj; ++j) {
+            const float4 *Sj = reinterpret_cast<const float4 *>(p.wsS + ((size_t)j * p.BH + bh) * kD * kD) + 64 * cw + l;
+            const float4 *Dj = reinterpret_cast<const float4 *>(p.wsA + ((size_t)j * p.BH + bh) * kD);
+            float4 x[16], d[16];
+#pragma unroll
+            for (int k4 = 0; k4 < 16; ++k4) {
+                x[k4] = Sj[256 * k4];
+                d[k4] = Dj[(32 * (k4 >> 2) + 8 * (k4 & 3) + 4 * h) >> 2];
+            }
+#pragma unroll
+            for (int k4 = 0; k4 < 16; ++k4) {
+                f32x16_t &A = S[k4 >> 2];
+                const int i = 4 * (k4 & 3);
+                A[i + 0] = fmaf(d[k4].x, A[i + 0], x[k4].x); A[i + 1] = fmaf(d[k4].y, A[i + 1], x[k4].y);
+                A[i + 2] = fmaf(d[k4].z, A[i + 2], x[k4].z); A[i + 3] = fmaf(d[k4].w, A[i + 3], x[k4].w);
+            }
+        }
+    } else {
+        // the combine's incoming state (lane-major)
+        const float4 *Sin = reinterpret_cast<const float4 *>(p.wsS + ((size_t)(seg * p.P - 1) * p.BH + bh) * kD * kD) +
+                            64 * cw + l;
+#pragma unroll
+        for (int k4 = 0; k4 < 16; ++k4) {
+            const float4 x = Sin[256 * k4];
+            f32x16_t &A = S[k4 >> 2];
+            const int i = 4 * (k4 & 3);
+            A[i + 0] = x.x; A[i + 1] = x.y; A[i + 2] = x.z; A[i + 3] = x.w;
+        }
     }
     for (int kk = 0; kk <= nch; ++kk) {
         if (kk >= 1) {
@@ -590,52 +629,57 @@ void scan_state_kernel(Params p) {
             state_chunk<TPR, LR>(Rb, Zb, ops, rzg, rzt, rs, t_begin + (c - 1) * CS,
                                  c >= 3 ? t_begin + (c - 3) * CS : -1, sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
     }
-    float *So = p.wsS + ((size_t)sub * p.BH + bh) * kD * kD;
+    float4 *So = reinterpret_cast<float4 *>(p.wsS + ((size_t)sub * p.BH + bh) * kD * kD) + 64 * w + l;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) So[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * kD + 32 * w + l32] = S[mt][i];
+    for (int k4 = 0; k4 < 16; ++k4) {
+        const f32x16_t &A = S[k4 >> 2];
+        const int i = 4 * (k4 & 3);
+        So[256 * k4] = make_float4(A[i + 0], A[i + 1], A[i + 2], A[i + 3]);
+    }
     if (r == 0) {
         float *A = p.wsA + ((size_t)sub * p.BH + bh) * kD + 8 * cg;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) A[e] = rho[e];
+        for (int e = 0; e < 8; ++e) A[e] = exp2_fast(rho[e]);
     }
 }
 
-// Phase 2: run the sub-segment states left to right,
-//   S <- diag(2^{A_j}) S + S_loc[j],
-// storing S into the slot of the last sub-segment of every segment (the
-// incoming state of the next segment).  One thread per (b,h, 4 consecutive
-// state elements of one row); all loads of a thread are independent and issued
-// up front.
+// Phase 2 when the output pass does not fold: run the sub-segment states left
+// to right, S <- diag(2^{A_j}) S + S_loc[j], storing S into the slot of the
+// last sub-segment of every segment (the incoming state of the next segment).
+// One thread per (b,h, float4 of the lane-major layout: 4 rows of one state
+// column); all loads of a thread are independent and issued up front.
 __global__ __launch_bounds__(256)
 void scan_combine_kernel(const float *__restrict__ S0, float *wsS, const float *__restrict__ wsA,
                          int BH, int nsub, int P) {
     const size_t idx4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
-    const size_t per4 = (size_t)kD * kD / 4;
+    constexpr size_t per4 = (size_t)kD * kD / 4;                 // 4096 float4 per state
     if (idx4 >= (size_t)BH * per4) return;
     const size_t bh = idx4 / per4;
-    const int i = (int)((idx4 % per4) / (kD / 4));
-    float4 s = S0 ? reinterpret_cast<const float4 *>(S0)[idx4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int rem = (int)(idx4 % per4), k4 = rem >> 8, lane = rem & 255;
+    const int w = lane >> 6, l = lane & 63;
+    const int row0 = 32 * (k4 >> 2) + 8 * (k4 & 3) + 4 * (l >> 5), col = 32 * w + (l & 31);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (S0) {
+        const float *b = S0 + bh * kD * kD + (size_t)row0 * kD + col;
+        s = make_float4(b[0], b[kD], b[2 * kD], b[3 * kD]);
+    }
     constexpr int kBatch = 8;
     for (int j0 = 0; j0 < nsub; j0 += kBatch) {
-        float4 x[kBatch];
-        float a[kBatch];
+        float4 x[kBatch], d[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int j = j0 + u;
             if (j < nsub) {
                 x[u] = reinterpret_cast<const float4 *>(wsS)[(size_t)j * BH * per4 + idx4];
-                a[u] = wsA[((size_t)j * BH + bh) * kD + i];
+                d[u] = *reinterpret_cast<const float4 *>(wsA + ((size_t)j * BH + bh) * kD + row0);
             }
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int j = j0 + u;
             if (j < nsub) {
-                const float d = exp2_fast(a[u]);
-                s.x = fmaf(d, s.x, x[u].x); s.y = fmaf(d, s.y, x[u].y);
-                s.z = fmaf(d, s.z, x[u].z); s.w = fmaf(d, s.w, x[u].w);
+                s.x = fmaf(d[u].x, s.x, x[u].x); s.y = fmaf(d[u].y, s.y, x[u].y);
+                s.z = fmaf(d[u].z, s.z, x[u].z); s.w = fmaf(d[u].w, s.w, x[u].w);
                 if ((j + 1) % P == 0) reinterpret_cast<float4 *>(wsS)[(size_t)j * BH * per4 + idx4] = s;
             }
         }
@@ -708,6 +752,7 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.wsS = (float *)a.workspace;
     p.wsA = p.wsS ? p.wsS + (size_t)nsub * BH * kD * kD : nullptr;
     p.BH = BH; p.T = a.T; p.G = q.G; p.seg_len = q.per_seg * a.chunk; p.P = q.P;
+    p.fold = nsub <= kFoldMax;
     p.sub_len = q.sub * a.chunk;
     p.cu = a.cu; p.H = a.H; p.total = a.total;
     p.order = a.cu ? a.order : nullptr;
@@ -719,9 +764,11 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
         if (lr) hipLaunchKernelGGL((scan_state_kernel<false, true>), g1, b1, 0, st, p);
         else if (vl) hipLaunchKernelGGL((scan_state_kernel<true, false>), g1, b1, 0, st, p);
         else hipLaunchKernelGGL((scan_state_kernel<false, false>), g1, b1, 0, st, p);
-        const size_t n4 = (size_t)BH * kD * kD / 4;
-        hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                           a.S0, p.wsS, p.wsA, BH, nsub, q.P);
+        if (!p.fold) {
+            const size_t n4 = (size_t)BH * kD * kD / 4;
+            hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                               a.S0, p.wsS, p.wsA, BH, nsub, q.P);
+        }
     }
     const dim3 grid(q.G * BH), blk(512);
     if (a.chunk == 64) {
