@@ -800,7 +800,7 @@ def main():
                    "dk": cfg["dk"], "dv": cfg["dv"], "chunk": cfg["chunk"],
                    "state_dtype": "fp32"},
         "roofline": _rl("hbm", pre["gbs"], HBM_PEAK_GBS, "GB/s", tr, pre["bytes"],
-                        kernel="rodimus_scan_prefill call (segment states + combine + output pass)",
+                        kernel="rodimus_scan_prefill call (segment states + output pass with the incoming states folded in)",
                         mfma_frac=round(pre["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                         cold_cache={"ms_median": round(pre["ms_cold_median"], 4),
                                     "ms_min": round(pre["ms_cold_min"], 4),
@@ -883,7 +883,7 @@ def main():
                 "ms_random_biases": round(lrk_rb["ms"], 4),
                 "roofline": _rl("hbm", lrk["gbs"], HBM_PEAK_GBS, "GB/s",
                                 measured_traffic("prefill_lowrank_1p6b_T4096", "prefill"), lrk["bytes"],
-                                kernel="rodimus_scan_prefill_lowrank call (segment states + combine + "
+                                kernel="rodimus_scan_prefill_lowrank call (segment states + "
                                        "output pass, gate logits from rank-16 factors in-kernel)")},
             "backward_1p6b_T4096": {
                 "ms": round(bw["ms"], 4), "ms_median": bw["ms_median"], "ms_min": bw["ms_min"],
