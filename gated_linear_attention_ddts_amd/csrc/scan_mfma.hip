@@ -13,9 +13,14 @@
 //     o  = Qt S  +  tril(Qt Kh^T) V         (MFMA, fp32 accumulation)
 //     S' = diag(2^{Lam[C-1]}) S + Kb^T V    (MFMA, fp32 accumulation)
 //
-// Kh needs 2^{-Lam} to stay inside the fp32/bf16 range: a chunk whose decay
-// span max_i(-Lam[C-1, i]) exceeds kSpan2 is processed token by token on the
-// VALU instead (same result).  Kb never overflows (its exponent is <= 0).
+// Kh needs 2^{-Lam} to stay inside the fp32/bf16 range.  A 64-token chunk is
+// therefore contracted as two 32-token halves, each with its own reference
+// (Lam restarts at the half's first token; Kb of the first half is taken to
+// the half's end): the first half's outputs, the state carried through the
+// first half, then the second half's outputs from that state, so that no
+// score tile spans both halves.  A chunk in which a half's decay span
+// max_i(-Lam[31, i]) exceeds kSpan2 is processed token by token on the VALU
+// instead (same result).  Kb never overflows (its exponent is <= 0).
 //
 // Segment-parallel form.  So that the grid fills the GPU when B*H is small, the
 // sequence of each (b, h) is cut into G segments (each a whole number of
@@ -76,8 +81,8 @@ constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 64 * kQRow * 2;
 constexpr int kOffKbT = kOffK + 64 * kQRow * 2;
 constexpr int kOffVT = kOffKbT + kD * kTRow * 2;
-constexpr int kOffGam = kOffVT + kD * kTRow * 2;
-constexpr int kBufBytes = kOffGam + kD * 4;
+constexpr int kOffGam = kOffVT + kD * kTRow * 2;   // 2^{decay} of each half: [2][128] fp32
+constexpr int kBufBytes = kOffGam + 2 * kD * 4;
 constexpr int kARow = 64 + 8;      // bf16 per row of sA [C][C] (token i, token j permuted)
 constexpr int kSABytes = 64 * kARow * 2;
 
@@ -214,16 +219,39 @@ void scan_full_kernel(Params p) {
                     if (more) load_gates<C, true>(R, rs, t0 + C, r, cg);
                 }
                 bool bad = false;
-                float gam[8];
+                float gam[8], gam1[8];  // 2^{decay} of the (first) half and of the second half
+                bool second = false;    // this lane's tokens are in the second half
+                if constexpr (NT == 2) {
+                    // each half against its own reference: Lam at the first half's
+                    // end (token 31, lane row 7) is taken off the second half's
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bad |= lend[e] < -kSpan2;
-                    gam[e] = exp2_fast(lend[e]);
+                    for (int e = 0; e < 8; ++e) {
+                        const float lmid = bcast_lane(l2a[TPR - 1][e], (l & 48) | 7);
+                        bad |= lmid < -kSpan2 || lend[e] - lmid < -kSpan2;
+                        gam[e] = exp2_fast(lmid);
+                        gam1[e] = exp2_fast(lend[e] - lmid);
+                        if (r >= 8) {
+#pragma unroll
+                            for (int tt = 0; tt < TPR; ++tt) l2a[tt][e] -= lmid;
+                        }
+                    }
+                    second = r >= 8;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        bad |= lend[e] < -kSpan2;
+                        gam[e] = exp2_fast(lend[e]);
+                        gam1[e] = 1.f;
+                    }
                 }
                 if (r == 0) {
                     float *sg = reinterpret_cast<float *>(buf + kOffGam) + 8 * cg;
                     *reinterpret_cast<float4 *>(sg) = make_float4(gam[0], gam[1], gam[2], gam[3]);
                     *reinterpret_cast<float4 *>(sg + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
+                    if (NT == 2) {
+                        *reinterpret_cast<float4 *>(sg + kD) = make_float4(gam1[0], gam1[1], gam1[2], gam1[3]);
+                        *reinterpret_cast<float4 *>(sg + kD + 4) = make_float4(gam1[4], gam1[5], gam1[6], gam1[7]);
+                    }
                 }
                 if (bad) sFlag[kk % 3] = 1;
                 if (tid == 0) sFlag[(kk + 1) % 3] = 0;
@@ -237,7 +265,7 @@ void scan_full_kernel(Params p) {
                     for (int e = 0; e < 8; ++e) {
                         qt[e] = qf[e] * exp2_fast(l2a[tt][e]);
                         kh[e] = kf[e] * exp2_fast(l2b[tt][e] - l2a[tt][e]);
-                        kbT[e][tt] = kh[e] * gam[e];
+                        kbT[e][tt] = kh[e] * (second ? gam1[e] : gam[e]);
                     }
                     const int t = TPR * r + tt;
                     store_q_row<kQRow>(buf + kOffQ, t, cg, qt);
@@ -425,15 +453,15 @@ void scan_full_kernel(Params p) {
                 bf16x8_t Sb[8];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) Sb[s] = cvt8(S[s >> 1], 8 * (s & 1));
-                // masked score tiles A^T[j][i] = Kh[j] . Qt[i] (j <= i); consumer wave ti
-                // builds tile (Jt, It) = (0,0), (0,1), (1,1) (only (0,0) for C = 32) and
-                // stores it as A[i][j] (j in permuted order) for all four waves
-                if (cw < (NT == 2 ? 3 : 1)) {
-                    const int Jt = (cw == 2) ? 1 : 0, It = (cw == 0) ? 0 : 1;
+                // masked score tiles A^T[j][i] = Kh[j] . Qt[i] (j <= i) of each half
+                // against its own reference: consumer wave cw builds the diagonal
+                // tile of half cw and stores it as A[i][j] (j in permuted order)
+                if (cw < NT) {
+                    const int It = cw;
                     f32x16_t at = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
-                        const bf16x8_t a = lds16(buf, kOffK + ((32 * Jt + l32) * kQRow + 16 * s + 8 * h) * 2);
+                        const bf16x8_t a = lds16(buf, kOffK + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2);
                         const bf16x8_t b = lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2);
                         at = mfma(a, b, at);
                     }
@@ -443,10 +471,10 @@ void scan_full_kernel(Params p) {
                         float x[4];
 #pragma unroll
                         for (int r4 = 0; r4 < 4; ++r4) {
-                            const int j = 32 * Jt + 8 * a4 + 4 * h + r4;
+                            const int j = 32 * It + 8 * a4 + 4 * h + r4;
                             x[r4] = (j <= i) ? at[4 * a4 + r4] : 0.f;
                         }
-                        *reinterpret_cast<uint2 *>(sA + (i * kARow + perm16(32 * Jt + 8 * a4 + 4 * h)) * 2) =
+                        *reinterpret_cast<uint2 *>(sA + (i * kARow + perm16(32 * It + 8 * a4 + 4 * h)) * 2) =
                             make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
                     }
                 }
@@ -454,17 +482,21 @@ void scan_full_kernel(Params p) {
                 // tiles that may be stale: this chunk's outputs are then written as
                 // NaN, never as silent garbage
                 const bool stale = consumer_barrier(sCBar, cbar_target, l);
-                // o^T tiles: 32 value channels (this wave's) x 32 tokens (32It..).  Same
-                // fragments as o = Qt S + A V with the operands swapped, so that a
-                // lane holds one token and 4 consecutive channels per register group.
-#pragma unroll
-                for (int It = 0; It < NT; ++It) {
+                const float *gam = reinterpret_cast<const float *>(buf + kOffGam);
+                // Per half: o^T tiles (32 value channels, this wave's, x 32 tokens) =
+                // S^T Qt^T + V^T A^T, the same fragments as o = Qt S + A V with the
+                // operands swapped, so that a lane holds one token and 4
+                // consecutive channels per register group; and the state through
+                // the half, S <- diag(gamma) S + Kb^T V.  For two halves the first
+                // half's state update is issued before its outputs (which use the
+                // bf16 state taken before it), so that its latency is hidden.
+                auto out = [&](int It) {
                     f32x16_t acc = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s)
                         acc = mfma(Sb[s], lds16(buf, kOffQ + ((32 * It + l32) * kQRow + 16 * s + 8 * h) * 2), acc);
 #pragma unroll
-                    for (int s = 0; s < 2 * It + 2; ++s)
+                    for (int s = 2 * It; s < 2 * It + 2; ++s)
                         acc = mfma(vB[s], lds16(sA, ((32 * It + l32) * kARow + 16 * s + 8 * h) * 2), acc);
                     const int t = t0 + 32 * It + l32;
                     if (t < t_end) {
@@ -479,20 +511,31 @@ void scan_full_kernel(Params p) {
                                       : make_uint2(pack2(acc[4 * a4 + 0], acc[4 * a4 + 1]),
                                                    pack2(acc[4 * a4 + 2], acc[4 * a4 + 3]));
                     }
-                }
-                // state: S <- diag(gamma) S + Kb^T V
-                const float *gam = reinterpret_cast<const float *>(buf + kOffGam);
+                };
+                auto adv = [&](int It) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
+                    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const float4 gm = *reinterpret_cast<const float4 *>(gam + 32 * mt + 8 * a4 + 4 * h);
-                        S[mt][4 * a4 + 0] *= gm.x; S[mt][4 * a4 + 1] *= gm.y;
-                        S[mt][4 * a4 + 2] *= gm.z; S[mt][4 * a4 + 3] *= gm.w;
+                        for (int a4 = 0; a4 < 4; ++a4) {
+                            const float4 gm = *reinterpret_cast<const float4 *>(gam + kD * It + 32 * mt + 8 * a4 + 4 * h);
+                            S[mt][4 * a4 + 0] *= gm.x; S[mt][4 * a4 + 1] *= gm.y;
+                            S[mt][4 * a4 + 2] *= gm.z; S[mt][4 * a4 + 3] *= gm.w;
+                        }
+#pragma unroll
+                        for (int s = 2 * It; s < 2 * It + 2; ++s)
+                            S[mt] = mfma(lds16(buf, kOffKbT + ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
                     }
+                };
+                if constexpr (NT == 2) {
+                    adv(0);
+                    out(0);
 #pragma unroll
-                    for (int s = 0; s < C / 16; ++s)
-                        S[mt] = mfma(lds16(buf, kOffKbT + ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
+                    for (int s = 0; s < 8; ++s) Sb[s] = cvt8(S[s >> 1], 8 * (s & 1));
+                    out(1);
+                    adv(1);
+                } else {
+                    out(0);
+                    adv(0);
                 }
             }
         }

@@ -104,6 +104,23 @@ def test_scan_reset_gates():
     check(x, 32, "fp32")
 
 
+@pytest.mark.parametrize("chunk", [64, 32])
+def test_scan_fast_decay_within_a_half(chunk):
+    """g ~ N(-2, 0.5), theta ~ N(2, 0.5): about 2.7 log2 units of decay per token,
+    so a 64-token chunk spans ~2^173 (beyond the factorised range) while each
+    32-token half spans ~2^86 (within it); a stretch of stronger decay (g ~ -4)
+    puts some halves beyond it too."""
+    B, H, T, dk, dv = 1, 3, 900, 128, 128
+    x = workloads.scan_inputs(17, B, H, T, dk, dv, "bf16")
+    rng = np.random.default_rng(9)
+    g = -2 + 0.5 * rng.standard_normal(x["g"].shape)
+    g[:, :, 500:560] -= 2.0
+    x["g"] = workloads.Tensor(workloads.round_to(g, "bf16"), "bf16")
+    x["theta"] = workloads.Tensor(workloads.round_to(2 + 0.5 * rng.standard_normal(x["g"].shape), "bf16"), "bf16")
+    log(f"scan fast decay C={chunk}")
+    check(x, chunk, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_scan_slow_decay(dtype):
     """g ~ N(4,1), theta ~ N(-2,1): a ~ 0.998, long-range carry across chunks."""
