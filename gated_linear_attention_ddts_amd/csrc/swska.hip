@@ -304,7 +304,7 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     if (ntile > 2) fetch_tile<D, NT>(kr, vr, kt0 + 2 * kBK, rk, rv);
 
     // One step: scores of tile j+1 (into Sn) beside the softmax and P V of
-    // tile j (from Sc), then tile j+2 to its buffer and tile j+3 in flight.
+    // tile j (from Sc), then tile j+2 to its buffer and tile j+3's loads issued.
     auto step = [&](int j, int bj, f32x16_t (&Sc)[2], f32x16_t (&Sn)[2]) {
         const int k0 = kt0 + j * kBK;
         const int b1 = bj == 2 ? 0 : bj + 1, b2 = b1 == 2 ? 0 : b1 + 1;
@@ -321,8 +321,10 @@ void swska_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             qk_tile<D, NT>(nb, qB, Sn, l32, h);
         }
         if (j + 2 < ntile) store_tile<D, NT>(smem + b2 * TL::BYTES, rk, rv);
-        __syncthreads();
+        // the staging registers are free again: tile j+3's loads go out before
+        // the barrier, so that the wait there overlaps their latency
         if (j + 3 < ntile) fetch_tile<D, NT>(kr, vr, k0 + 3 * kBK, rk, rv);
+        __syncthreads();
         return b1;
     };
     f32x16_t Sa[2], Sb[2];
