@@ -497,7 +497,9 @@ void bwd_grad_kernel(P p) {
         sX2[t * kSR + rr] = ax[i];
     }
     if (h == 0) sDec[rr] = dec;
-    // the epilogue's inputs again (L2-resident), once the accumulators are free
+    // the epilogue's g and tau again (L2-resident), once the accumulators are
+    // free; q and k stay in the registers of the first load (kept through the
+    // products: 16 VGPRs more, no spills, where also keeping g and tau spills)
     uint4 Eq[2], Ek[2], Eg[2], Eth[2];
     load_one<2>(Eg, rg, t0, r, cg);
     load_one<2>(Eth, rth, t0, r, cg);
@@ -509,8 +511,11 @@ void bwd_grad_kernel(P p) {
     float l2a[2][8], l2b[2][8], lend[8];
     gates_scan_gt<kSub>(Eg, Eth, t0, len, r, l, l2a, l2b, lend);
     __builtin_amdgcn_sched_barrier(0);
-    load_one<2>(Eq, rq, t0, r, cg);
-    load_one<2>(Ek, rk, t0, r, cg);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        Eq[i] = Rq[i];
+        Ek[i] = Rk[i];
+    }
     float dlam[2][8], dmu[2][8], ebs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ebs[e] = 0.f;
