@@ -310,6 +310,17 @@ void bwd_grad_kernel(P p) {
     load_one<2>(Rk, rk, t0, r, cg);
     load_one<2>(Rv, rv, t0, r, cg);
     load_one<2>(Rdo, rdo, t0, r, cg);
+    // the chunk's two checkpoints (S entering, G leaving), in flight while the
+    // gate map and the operand rows are built
+    uint4 rS[8], rG[8];
+    {
+        const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            rS[s] = ld_raw(cS, 8 * w + s, l);
+            rG[s] = ld_raw(cG, 8 * w + s, l);
+        }
+    }
 
     // this chunk's gates; span check (Kh = k 2^{mu - Lam} must stay finite)
     uint32_t qTp[8], kTp[8];  // Qt^T / Kh^T rows of this lane's 8 channels, 2 tokens packed
@@ -359,13 +370,7 @@ void bwd_grad_kernel(P p) {
     // later / earlier segments completed with the segment fix-up
     bf16x8_t Sf[8], Gf[8], GTf[8];
     {
-        const bf16_t *cS = p.ckS + ck * kFrag, *cG = p.ckG + ck * kFrag;
-        uint4 rS[8], rG[8], fS[8], fG[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            rS[s] = ld_raw(cS, 8 * w + s, l);
-            rG[s] = ld_raw(cG, 8 * w + s, l);
-        }
+        uint4 fS[8], fG[8];
         const float sigS = fixS ? p.sigS[ck * kD + rr] : 0.f;
         const float sigG = fixG ? p.sigG[ck * kD + rr] : 0.f;
         if (fixS) {
