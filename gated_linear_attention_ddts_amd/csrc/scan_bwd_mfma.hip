@@ -205,29 +205,53 @@ void bwd_state_kernel(P p) {
 }
 
 // ----------------------------------------------------------------- combine
-// One thread per (b,h, r, n): the state entering each segment (left to right)
-// and the gradient leaving each segment (right to left), stored bf16 in
-// fragment order for the gradient kernel; the gradient entering segment 0 is
-// dS0.
+// The state entering each segment (left to right) and the gradient leaving
+// each segment (right to left), stored bf16 in fragment order for the gradient
+// kernel; the gradient entering segment 0 is dS0.  One thread per (b,h,
+// fragment slot): the 8 values one lane holds of one operand fragment, which
+// frag_index places at row r, columns c0..c0+3 and c0+8..c0+11, so that each
+// load is a 16-byte run of a row and each store one 16-byte slot.
 __global__ __launch_bounds__(256)
 void bwd_combine_kernel(P p) {
+    constexpr int kSlots = kFrag / 8;  // 2048 per 128 x 128 matrix
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)p.BH * kD * kD) return;
-    const int bh = (int)(idx >> 14), e = (int)(idx & 16383), r = e >> 7, n = e & 127;
-    const int fi = frag_index(r, n);
-    float S = 0.f;
+    if (idx >= (size_t)p.BH * kSlots) return;
+    const int bh = (int)(idx / kSlots), slot = (int)(idx % kSlots);
+    const int f = slot >> 6, ln = slot & 63;
+    const int r = 32 * (f >> 3) + (ln & 31), c0 = 16 * (f & 7) + 4 * (ln >> 5);
+    auto row8 = [&](const float *m, float (&x)[8]) {
+        const float4 a = *reinterpret_cast<const float4 *>(m + r * kD + c0);
+        const float4 b = *reinterpret_cast<const float4 *>(m + r * kD + c0 + 8);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    };
+    auto put = [&](bf16_t *m, const float (&x)[8]) {
+        *reinterpret_cast<uint4 *>(m + (size_t)slot * 8) =
+            make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+    };
+    float S[8], G[8], x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S[e] = G[e] = 0.f;
     for (int s = 0; s < p.nseg; ++s) {
         const size_t sb = (size_t)bh * p.nseg + s;
-        if (s > 0) p.fixS[sb * kFrag + fi] = f2bf(S);
-        S = fmaf(exp2_fast(p.segDS[sb * kD + r]), S, p.segS[sb * kD * kD + e]);
+        if (s > 0) put(p.fixS + sb * kFrag, S);
+        const float d = exp2_fast(p.segDS[sb * kD + r]);
+        row8(p.segS + sb * kD * kD, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[e] = fmaf(d, S[e], x[e]);
     }
-    float G = 0.f;
     for (int s = p.nseg - 1; s >= 0; --s) {
         const size_t sb = (size_t)bh * p.nseg + s;
-        if (s < p.nseg - 1) p.fixG[sb * kFrag + fi] = f2bf(G);
-        G = fmaf(exp2_fast(p.segDG[sb * kD + r]), G, p.segG[sb * kD * kD + e]);
+        if (s < p.nseg - 1) put(p.fixG + sb * kFrag, G);
+        const float d = exp2_fast(p.segDG[sb * kD + r]);
+        row8(p.segG + sb * kD * kD, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) G[e] = fmaf(d, G[e], x[e]);
     }
-    if (p.dS0) p.dS0[idx] = G;
+    if (p.dS0) {
+        float *o = p.dS0 + (size_t)bh * kD * kD + r * kD + c0;
+        *reinterpret_cast<float4 *>(o) = make_float4(G[0], G[1], G[2], G[3]);
+        *reinterpret_cast<float4 *>(o + 8) = make_float4(G[4], G[5], G[6], G[7]);
+    }
 }
 
 // ---------------------------------------------------------- gradient kernel
@@ -686,7 +710,7 @@ uint64_t scan_bwd_mfma_launch_items(long long BH, int T) {
     if (BH <= 0 || T <= 0) return 0;
     const Plan q = plan(BH, T);
     uint64_t m = (uint64_t)2 * BH * q.nseg * 256;                               // state passes
-    if (q.nseg > 1) m = std::max<uint64_t>(m, (uint64_t)BH * kD * kD);          // combine
+    if (q.nseg > 1) m = std::max<uint64_t>(m, (uint64_t)BH * (kFrag / 8));      // combine
     m = std::max<uint64_t>(m, (uint64_t)BH * q.nck * 256);                      // gradients
     return std::max<uint64_t>(m, (uint64_t)kSlowWG * 256);                      // fallback
 }
@@ -712,7 +736,7 @@ void launch_scan_bwd_mfma(const ScanBwdArgs &a, hipStream_t st) {
     p.order = a.cu ? a.order : nullptr;
     hipLaunchKernelGGL(bwd_state_kernel, dim3((unsigned)(2 * BH * q.nseg)), dim3(256), 0, st, p);
     if (q.nseg > 1) {
-        const size_t n = (size_t)BH * kD * kD;
+        const size_t n = (size_t)BH * (kFrag / 8);
         hipLaunchKernelGGL(bwd_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
     }
     hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)((size_t)BH * q.nck)), dim3(256), 0, st, p);
