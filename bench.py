@@ -722,6 +722,27 @@ def cpu_baseline_long(cfg, T_sample=16384):
                        f"{dt:.2f} s wall, {cpu:.1f} s CPU")
 
 
+def cpu_baseline_backward(cfg, T_sample=1024):
+    """The oracle's backward (the gradients of the sequential recurrence, fp64 C
+    loops, one (b,h) per thread) on every head of the first sequence over its
+    first T_sample tokens."""
+    import oracle
+    import workloads
+    cores = _oracle_cores()
+    H, dk, dv = cfg["H"], cfg["dk"], cfg["dv"]
+    x = workloads.scan_inputs(cfg["seed"], 1, H, T_sample, dk, dv, cfg["dtype"], gate_mu=cfg["gate_mu"])
+    arrs = [x[n].f64() for n in NAMES]
+    del x
+    dO = np.random.default_rng(cfg["seed"] + 1000).standard_normal((1, H, T_sample, dv))
+    c0, t0 = time.process_time(), time.perf_counter()
+    oracle.scan_backward(*arrs, dO, nthreads=cores)
+    dt, cpu = time.perf_counter() - t0, time.process_time() - c0
+    return dict(value=round(T_sample / dt, 1), unit="tokens/s", cores=min(cores, H), kind="oracle",
+                sample=f"all {H} heads of one sequence over its first {T_sample} of the {cfg['T']} tokens, "
+                       f"fp64 gradients of the sequential recurrence, one (b,h) per thread: {dt:.2f} s wall, "
+                       f"{cpu:.1f} s CPU; a token is all {H} heads")
+
+
 def cpu_baseline_decode(cfg, steps=6):
     """The oracle's decode step (single-threaded C loop) over the whole batch of
     N sequences x H heads, for `steps` steps from zero states."""
@@ -854,13 +875,14 @@ def main():
     stage("backward_varlen_N64_16K")
     bvl = bench_backward_varlen(workloads.CONFIGS["prefill_varlen_N64_16K"], max(5, args.steps // 2), 2)
 
-    cpu = cpu_long = cpu_dec = cpu_ska = None
+    cpu = cpu_long = cpu_dec = cpu_ska = cpu_bwd = None
     if not args.no_cpu:
         stage("cpu baselines (fp64 oracle)")
         cpu = cpu_baseline(cfg)
         cpu_long = cpu_baseline_long(lc)
         cpu_dec = cpu_baseline_decode(workloads.CONFIGS["decode_N256"])
         cpu_ska = cpu_baseline_swska(sc)
+        cpu_bwd = cpu_baseline_backward(cfg)
 
     tr = measured_traffic("prefill_1p6b_T4096", "prefill")
     dtr = measured_traffic("decode_N256", "decode")
@@ -977,7 +999,8 @@ def main():
                 "roofline": _rl("hbm", bw["gbs"], HBM_PEAK_GBS, "GB/s",
                                 measured_traffic("backward_1p6b_T4096", "backward"), bw["bytes"],
                                 kernel="rodimus_scan_backward call (state passes + combine + gradients + fallback)",
-                                workspace_bytes=bw["workspace_bytes"])},
+                                workspace_bytes=bw["workspace_bytes"]),
+                "cpu_baseline": cpu_bwd},
             "prefill_varlen_N64_16K": {
                 "ms": round(vl["ms"], 4), "ms_median": vl["ms_median"], "ms_min": vl["ms_min"],
                 "tokens_per_s": round(vl["tokens_per_s"]),
