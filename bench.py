@@ -18,17 +18,17 @@ Timing: W untimed warm-up steps, then K steps between two HIP events on the
 stream the kernels run on (torch's current stream), with device syncs on both
 sides and no event between the steps (an event between two kernels costs about
 10 us here).  The per-call median and minimum come from a separate run of
-batches of calls, each batch between two events and at least 1 ms long.  One prefill call launches up to three kernels (segment states, their
-combination, the output pass); the roofline entry is for that whole call.
+batches of calls, each batch between two events and at least 1 ms long.  One
+prefill call launches up to three kernels (segment states, their combination,
+the output pass); the roofline entry is for that whole call.
 
 A GPU that has just been idle runs the first tens of milliseconds of any load
 below the clock it holds under sustained load (at W = 5 the headline comes out
 about 10% slower, SW-SKA about 25%).  So the headline's W warm-up steps are
 preceded by about 200 ms of a neutral load, bf16 matrix products on torch (the
 "precondition" field), and the same K steps timed before it are reported as
-"clock_rising".
-Every other workload warms up on its own calls for at least 200 ms
-("warmup_calls").
+"clock_rising".  Every other workload warms up on its own calls for at least
+200 ms ("warmup_calls").
 
 Algorithmic bytes: prefill, per token-head, q, k, g, tau (4 x 256 B) + v (256 B)
 in and o (256 B) out = 1536 B, plus the fp32 final state; decode, per head, the
