@@ -53,7 +53,7 @@ def _f64(a):
     return None if a is None else a.astype(np.float64)
 
 
-@pytest.mark.parametrize("c", _scan_cases(16, 71, 700), ids=_scan_id)
+@pytest.mark.parametrize("c", _scan_cases(40, 71, 700), ids=_scan_id)
 def test_prefill_random_shape(c):
     log(f"prefill {_scan_id(c)} S0={c['S0']}")
     x = workloads.scan_inputs(c["seed"], c["B"], c["H"], c["T"], c["dk"], c["dv"], c["dtype"], gate_mu=c["gate_mu"])
@@ -67,7 +67,7 @@ def test_prefill_random_shape(c):
     assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
 
 
-@pytest.mark.parametrize("c", _scan_cases(10, 72, 400),
+@pytest.mark.parametrize("c", _scan_cases(24, 72, 400),
                          ids=lambda c: f"{c['dtype']}-B{c['B']}H{c['H']}T{c['T']}-{c['dk']}x{c['dv']}-mu{c['gate_mu']}")
 def test_backward_random_shape(c):
     log(f"backward {c}")
@@ -99,7 +99,7 @@ def _decode_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("c", _decode_cases(8, 73),
+@pytest.mark.parametrize("c", _decode_cases(16, 73),
                          ids=lambda c: f"{c['dtype']}-N{c['N']}H{c['H']}-{c['dk']}x{c['dv']}-s{c['steps']}")
 def test_decode_random_shape(c):
     log(f"decode {c}")
@@ -135,7 +135,7 @@ def _ska_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("c", _ska_cases(10, 74),
+@pytest.mark.parametrize("c", _ska_cases(20, 74),
                          ids=lambda c: f"D{c['D']}-B{c['B']}H{c['H']}T{c['T']}-w{c['window']}")
 def test_swska_random_shape(c):
     log(f"sw-ska {c}")
@@ -160,7 +160,7 @@ def _ska_decode_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("c", _ska_decode_cases(10, 75),
+@pytest.mark.parametrize("c", _ska_decode_cases(20, 75),
                          ids=lambda c: f"D{c['D']}-N{c['N']}H{c['H']}-W{c['W']}")
 def test_swska_decode_random_shape(c):
     log(f"sw-ska decode {c}")
