@@ -281,6 +281,88 @@ __device__ __forceinline__ void chunk_scan(int t0, int tend, int r, int l, float
     }
 }
 
+// gfx950's row swaps with one value in both operands.  v_permlane16_swap
+// exchanges the odd 16-lane rows of one operand with the even rows of the
+// other, v_permlane32_swap the upper 32 lanes of one with the lower 32 of the
+// other: every lane receives x at its own position in rows (row & 2) and
+// (row & 2) + 1, or in lanes l mod 32 and 32 + l mod 32.
+
+__device__ __forceinline__ void row_pair16(float x, float &even, float &odd) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    even = __uint_as_float(p[0]);
+    odd = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void row_pair32(float x, float &lo, float &hi) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(p[0]);
+    hi = __uint_as_float(p[1]);
+}
+
+// In-chunk scan for the producer layout by halves of a 64-token chunk: wave
+// pair w >> 1 holds one 32-token half, lane block i = l >> 3 its tokens
+// 4i .. 4i+3 of the half (lanes 8 apart), lane l & 7 a channel group, so that
+// each load instruction reads 128 contiguous bytes of 8 token rows.  Each
+// half is scanned from its own first token (the exponent reference of its
+// products): on return l2a holds Lam from the half's first token (inclusive),
+// l2b log2 beta, htot the half's total, per channel.  Blocks 2k, 2k+1 share a
+// 16-lane row: their prefix comes from a row shift by 8, the rows' totals from
+// the two row swaps.  Tokens at or beyond tend get a = 1, beta = 0.
+template <int C>
+__device__ __forceinline__ void chunk_scan_half(int t0, int tend, int r, int l, float (&l2a)[C / 16][8],
+                                                float (&l2b)[C / 16][8], float (&htot)[8]) {
+    static_assert(C == 64, "halves of 64-token chunks");
+    constexpr int TPR = C / 16;
+    if (t0 + C > tend) {  // ragged last chunk
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt)
+            if (t0 + TPR * r + tt >= tend) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { l2a[tt][e] = 0.f; l2b[tt][e] = -INFINITY; }
+            }
+    }
+#pragma unroll
+    for (int tt = 1; tt < TPR; ++tt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) l2a[tt][e] += l2a[tt - 1][e];
+    const bool odd = (l >> 3) & 1;
+    const int row = l >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // Every cross-lane read here feeds arithmetic that all lanes run: a
+        // read whose only use is one arm of a lane-dependent select can be
+        // moved under a branch, where the lanes it reads from are switched
+        // off and yield 0.  The two shifts fill 0 across the row's edge, so
+        // both blocks of a row get the same sum, added in the same order.
+        const float x = l2a[TPR - 1][e];  // this block's total
+        const float t = row_shr<8>(x);    // the even block's, in the odd block; 0 in the even one
+        const float u = row_shl<8>(x);    // the odd block's, in the even block; 0 in the odd one
+        const float rt = (x + t) + u;     // the row's two blocks
+        float re, ro, plo, phi;
+        row_pair16(rt, re, ro);
+        row_pair32(re + ro, plo, phi);
+        const float excl = ((row & 1) ? re : 0.f) + ((row & 2) ? plo : 0.f) + t;
+        htot[e] = plo + phi;
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) l2a[tt][e] += excl;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void gates_scan_half(const uint4 (&G)[C / 16], const uint4 (&TH)[C / 16], int t0,
+                                                int tend, int r, int l, float (&l2a)[C / 16][8],
+                                                float (&l2b)[C / 16][8], float (&htot)[8]) {
+    constexpr int TPR = C / 16;
+#pragma unroll
+    for (int tt = 0; tt < TPR; ++tt) {
+        float gf[8], tf[8];
+        unpack8(G[tt], gf);
+        unpack8(TH[tt], tf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ddts_log2_gates_fast(gf[e], tf[e], l2a[tt][e], l2b[tt][e]);
+    }
+    chunk_scan_half<C>(t0, tend, r, l, l2a, l2b, htot);
+}
+
 // Gates and in-chunk inclusive scan: on return l2a holds Lam (inclusive
 // cumulative log2 a), l2b log2 beta, lend the chunk total Lam[C-1] of each of
 // the lane's 8 channels.  Tokens at or beyond tend get a = 1, beta = 0.

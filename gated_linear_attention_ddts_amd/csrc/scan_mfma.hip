@@ -167,7 +167,15 @@ void scan_full_kernel(Params p) {
 
     if (w < 4) {
         // ======================= producers =======================
-        const int r = l & 15, cg = (w << 2) | (l >> 4);
+        // Lane (r, cg) holds tokens TPR r .. TPR r + TPR - 1 of the chunk for
+        // channels 8 cg .. 8 cg + 7.  For the full-rank 64-token chunks the
+        // wave pairs take the halves (r = 8 (w >> 1) + (l >> 3), cg = 8 (w & 1) +
+        // (l & 7)), so that each load instruction reads 8 rows of 128 bytes, and
+        // each half is scanned inside its waves; otherwise the 16 lanes of a row
+        // hold the whole chunk of one channel group (16 rows of 64 bytes).
+        constexpr bool kHalves = C == 64 && !LR;
+        const int r = kHalves ? 8 * (w >> 1) + (l >> 3) : l & 15;
+        const int cg = kHalves ? 8 * (w & 1) + (l & 7) : (w << 2) | (l >> 4);
         Rsrc rs;
         rs.q = rsrc(p.q + rowbase * kD, Tb); rs.k = rsrc(p.k + rowbase * kD, Tb);
         rs.v = rsrc(p.v + rowbase * kD, Tb);
@@ -215,13 +223,22 @@ void scan_full_kernel(Params p) {
                 } else {
                     store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);
                     if (more) load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
-                    gates_scan_gt<C>(R.g, R.th, t0, t_end, r, l, l2a, l2b, lend);
+                    if constexpr (kHalves) gates_scan_half<C>(R.g, R.th, t0, t_end, r, l, l2a, l2b, lend);
+                    else gates_scan_gt<C>(R.g, R.th, t0, t_end, r, l, l2a, l2b, lend);
                     if (more) load_gates<C, true>(R, rs, t0 + C, r, cg);
                 }
                 bool bad = false;
                 float gam[8], gam1[8];  // 2^{decay} of the (first) half and of the second half
                 bool second = false;    // this lane's tokens are in the second half
-                if constexpr (NT == 2) {
+                if constexpr (kHalves) {
+                    // lend is this wave pair's half total, Lam already from the half's start
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        bad |= lend[e] < -kSpan2;
+                        gam[e] = exp2_fast(lend[e]);
+                    }
+                    second = r >= 8;
+                } else if constexpr (NT == 2) {
                     // each half against its own reference: Lam at the first half's
                     // end (token 31, lane row 7) is taken off the second half's
 #pragma unroll
@@ -244,11 +261,12 @@ void scan_full_kernel(Params p) {
                         gam1[e] = 1.f;
                     }
                 }
-                if (r == 0) {
-                    float *sg = reinterpret_cast<float *>(buf + kOffGam) + 8 * cg;
+                if (kHalves ? (r & 7) == 0 : r == 0) {
+                    // by halves: each wave pair writes its own half's factor
+                    float *sg = reinterpret_cast<float *>(buf + kOffGam) + 8 * cg + (kHalves && second ? kD : 0);
                     *reinterpret_cast<float4 *>(sg) = make_float4(gam[0], gam[1], gam[2], gam[3]);
                     *reinterpret_cast<float4 *>(sg + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
-                    if (NT == 2) {
+                    if (!kHalves && NT == 2) {
                         *reinterpret_cast<float4 *>(sg + kD) = make_float4(gam1[0], gam1[1], gam1[2], gam1[3]);
                         *reinterpret_cast<float4 *>(sg + kD + 4) = make_float4(gam1[4], gam1[5], gam1[6], gam1[7]);
                     }
@@ -265,7 +283,7 @@ void scan_full_kernel(Params p) {
                     for (int e = 0; e < 8; ++e) {
                         qt[e] = qf[e] * exp2_fast(l2a[tt][e]);
                         kh[e] = kf[e] * exp2_fast(l2b[tt][e] - l2a[tt][e]);
-                        kbT[e][tt] = kh[e] * (second ? gam1[e] : gam[e]);
+                        kbT[e][tt] = kh[e] * (!kHalves && second ? gam1[e] : gam[e]);
                     }
                     const int t = TPR * r + tt;
                     store_q_row<kQRow>(buf + kOffQ, t, cg, qt);
