@@ -324,7 +324,6 @@ __device__ __forceinline__ void chunk_scan_half(int t0, int tend, int r, int l, 
     for (int tt = 1; tt < TPR; ++tt)
 #pragma unroll
         for (int e = 0; e < 8; ++e) l2a[tt][e] += l2a[tt - 1][e];
-    const bool odd = (l >> 3) & 1;
     const int row = l >> 4;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
