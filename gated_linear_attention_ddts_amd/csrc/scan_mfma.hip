@@ -73,6 +73,10 @@ namespace {
 constexpr int kCUs = 256;
 constexpr int kFoldMax = 8;        // sub-segment states a consumer wave folds itself
 constexpr int kMaxT = 1 << 23;     // 32-bit buffer offsets (T * 256 bytes)
+// A chunk start whose rows lie past the end of every descriptor (T < kMaxT):
+// loads from it return zeros and fetch nothing, and its byte offsets, up to
+// (kMaxT + 63) * 256 + 240, still fit 32 bits.
+constexpr int kNoRow = kMaxT;
 
 // LDS buffer layout (bytes); rows padded by 16 bytes (conflict-free 16-byte reads)
 constexpr int kQRow = kD + 8;      // bf16 per row of sQ / sK       [C][128]
@@ -595,10 +599,14 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1>
         }
         gates_scan_cols<16 * TPR>(gw, tw, t0, T, r, l, l2a, l2b, lend);
     } else {
+        // (full rank: the prefetches are always issued, from past the rows'
+        // end when there is no next chunk, in the order of the first loads,
+        // so that each wait of the load counter is exact)
+        const int tn = tnext >= 0 ? tnext : kNoRow;
         store_vt<TPR, kTRow>(sVT, cg, r, R.v);
-        if (tnext >= 0) load_one<TPR>(R.v, rs.v, tnext, r, cg);
+        load_one<TPR>(R.v, rs.v, tn, r, cg);
         gates_scan_gt<16 * TPR>(R.g, R.th, t0, T, r, l, l2a, l2b, lend);
-        if (tnext >= 0) load_gates<16 * TPR, false>(R, rs, tnext, r, cg);
+        load_gates<16 * TPR, false>(R, rs, tn, r, cg);
     }
     float kbT[8][TPR];
 #pragma unroll
@@ -611,7 +619,7 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1>
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) rho[e] += lend[e];
-    if (tnext >= 0) load_one<TPR>(R.k, rs.k, tnext, r, cg);
+    if (!LR || tnext >= 0) load_one<TPR>(R.k, rs.k, tnext >= 0 ? tnext : kNoRow, r, cg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) store_t_rows<TPR, kTRow>(sKbT, 8 * cg + e, r, kbT[e]);
     __syncthreads();
@@ -675,13 +683,25 @@ void scan_state_kernel(Params p) {
     Raw<CS, false, LR> Ra, Rb;
     Zops<1> Za, Zb;
     const int c0 = nch - 1;
-    if (c0 >= 0) {
-        load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
-        if constexpr (LR) load_zops<1>(Za, rzg, rzt, t_begin + c0 * CS, l);
-    }
-    if (c0 >= 1) {
-        load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
-        if constexpr (LR) load_zops<1>(Zb, rzg, rzt, t_begin + (c0 - 1) * CS, l);
+    if constexpr (LR) {
+        if (c0 >= 0) {
+            load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
+            load_zops<1>(Za, rzg, rzt, t_begin + c0 * CS, l);
+        }
+        if (c0 >= 1) {
+            load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
+            load_zops<1>(Zb, rzg, rzt, t_begin + (c0 - 1) * CS, l);
+        }
+    } else {
+        // the first two chunks in the order of the loop's prefetches (v, then
+        // g and th, then k), always issued
+        const int ta = c0 >= 0 ? t_begin + c0 * CS : kNoRow, tb = c0 >= 1 ? t_begin + (c0 - 1) * CS : kNoRow;
+        load_one<TPR>(Ra.v, rs.v, ta, r, cg);
+        load_gates<CS, false>(Ra, rs, ta, r, cg);
+        load_one<TPR>(Ra.k, rs.k, ta, r, cg);
+        load_one<TPR>(Rb.v, rs.v, tb, r, cg);
+        load_gates<CS, false>(Rb, rs, tb, r, cg);
+        load_one<TPR>(Rb.k, rs.k, tb, r, cg);
     }
     for (int c = c0; c >= 0; c -= 2) {
         state_chunk<TPR, LR>(Ra, Za, ops, rzg, rzt, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1,
