@@ -398,14 +398,6 @@ __device__ __forceinline__ void gates_scan_cols(const uint32_t (&gw)[8][C / 32],
     chunk_scan<C>(t0, tend, r, l, l2a, l2b, lend);
 }
 
-// Forces the raw registers of a chunk to have arrived here (an empty asm that
-// reads them), before the next chunk's prefetches are issued: a wait placed
-// after those prefetches would, with the in-order load counter, wait for them
-// too and expose a whole memory latency per chunk.
-__device__ __forceinline__ void arrived(const uint4 &x) {
-    __asm__ volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
-}
-
 // Row c of Kb^T / V^T: tokens TPR*r .. TPR*r+TPR-1 at their permuted position.
 template <int TPR, int ROW>
 __device__ __forceinline__ void store_t_rows(char *base, int c, int r, const float *x) {

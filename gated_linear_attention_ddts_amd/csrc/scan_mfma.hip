@@ -193,24 +193,33 @@ void scan_full_kernel(Params p) {
             rzg = rsrc_bytes(p.zg + zrow * kRank, Tb * (int)kZRow);
             rzt = rsrc_bytes(p.zt + zrow * kRank, Tb * (int)kZRow);
             lr_load_ops(ops, p.Ug, p.bg, p.Ut, p.bt, bh % p.H, w, l);
-            load_zops<NT>(Z, rzg, rzt, t_begin, l);
         } else {
             rs.g = rsrc(p.g + rowbase * kD, Tb);
             rs.th = rsrc(p.th + rowbase * kD, Tb);
         }
         Raw<C, true, LR> R;
-        load_raw<C, true>(R, rs, t_begin, r, cg);
+        if constexpr (LR) {
+            // Low rank: the first chunk in the order of the loop's prefetches
+            // (v, the factor rows, then q and k), and the prefetches always
+            // issued (from past the rows' end after the last chunk), so that
+            // each wait of the in-order load counter is exact: the factor rows
+            // are waited for without q and k, which are needed only after the
+            // gate map.
+            load_one<TPR>(R.v, rs.v, t_begin, r, cg);
+            load_zops<NT>(Z, rzg, rzt, t_begin, l);
+            load_one<TPR>(R.q, rs.q, t_begin, r, cg);
+            load_one<TPR>(R.k, rs.k, t_begin, r, cg);
+        } else {
+            load_raw<C, true>(R, rs, t_begin, r, cg);
+        }
         for (int kk = 0; kk <= nch; ++kk) {
             if (kk < nch) {
                 const int t0 = t_begin + kk * C;
                 char *buf = smem + (kk & 1) * kBufBytes;
                 const bool more = kk + 1 < nch;
                 float l2a[TPR][8], l2b[TPR][8], lend[8];
+                const int tn = more ? t0 + C : kNoRow;  // low rank: the next chunk's loads
                 if constexpr (LR) {
-                    // every raw input of this chunk has arrived before any
-                    // prefetch of the next one is issued
-#pragma unroll
-                    for (int tt = 0; tt < TPR; ++tt) { arrived(R.q[tt]); arrived(R.k[tt]); arrived(R.v[tt]); }
                     // logits on the matrix cores, staged in this wave's rows of
                     // the K-bar^T (g) and V^T (tau) areas, read back per lane
                     lr_stage<NT, kTRow>(Z, ops, buf + kOffKbT, buf + kOffVT, w, l);
@@ -219,10 +228,8 @@ void scan_full_kernel(Params p) {
                     uint32_t gw[8][TPR / 2], tw[8][TPR / 2];
                     lr_read<TPR, kTRow>(buf + kOffKbT, buf + kOffVT, r, cg, gw, tw);
                     store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);   // after the reads, in LDS order
-                    if (more) {
-                        load_one<TPR>(R.v, rs.v, t0 + C, r, cg);
-                        load_zops<NT>(Z, rzg, rzt, t0 + C, l);
-                    }
+                    load_one<TPR>(R.v, rs.v, tn, r, cg);
+                    load_zops<NT>(Z, rzg, rzt, tn, l);
                     gates_scan_cols<C>(gw, tw, t0, t_end, r, l, l2a, l2b, lend);
                 } else {
                     store_vt<TPR, kTRow>(buf + kOffVT, cg, r, R.v);
@@ -293,9 +300,9 @@ void scan_full_kernel(Params p) {
                     store_q_row<kQRow>(buf + kOffQ, t, cg, qt);
                     store_q_row<kQRow>(buf + kOffK, t, cg, kh);
                 }
-                if (more) {
-                    load_one<TPR>(R.q, rs.q, t0 + C, r, cg);
-                    load_one<TPR>(R.k, rs.k, t0 + C, r, cg);
+                if (LR || more) {
+                    load_one<TPR>(R.q, rs.q, LR ? tn : t0 + C, r, cg);
+                    load_one<TPR>(R.k, rs.k, LR ? tn : t0 + C, r, cg);
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) store_t_rows<TPR, kTRow>(buf + kOffKbT, 8 * cg + e, r, kbT[e]);
@@ -582,9 +589,11 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1>
                                             int t0, int tnext, char *sKbT, char *sVT, f32x16_t (&S)[4],
                                             float (&rho)[8], int r, int cg, int l, int w, int h, int l32, int T) {
     float l2a[TPR][8], l2b[TPR][8], lend[8];
+    // The prefetches are always issued, from past the rows' end when there is
+    // no next chunk, in the order of the first loads (v, then the gate inputs,
+    // then k), so that each wait of the in-order load counter is exact.
+    const int tn = tnext >= 0 ? tnext : kNoRow;
     if constexpr (LR) {
-#pragma unroll
-        for (int tt = 0; tt < TPR; ++tt) { arrived(R.k[tt]); arrived(R.v[tt]); }
         // logits of the 32-token chunk on the matrix cores, staged in this
         // wave's rows of the K-bar^T (g) and V^T (tau) areas
         lr_stage<1, kTRow>(Z, ops, sKbT, sVT, w, l);
@@ -593,16 +602,10 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1>
         uint32_t gw[8][TPR / 2], tw[8][TPR / 2];
         lr_read<TPR, kTRow>(sKbT, sVT, r, cg, gw, tw);
         store_vt<TPR, kTRow>(sVT, cg, r, R.v);   // after the reads, in LDS order
-        if (tnext >= 0) {
-            load_one<TPR>(R.v, rs.v, tnext, r, cg);
-            load_zops<1>(Z, rzg, rzt, tnext, l);
-        }
+        load_one<TPR>(R.v, rs.v, tn, r, cg);
+        load_zops<1>(Z, rzg, rzt, tn, l);
         gates_scan_cols<16 * TPR>(gw, tw, t0, T, r, l, l2a, l2b, lend);
     } else {
-        // (full rank: the prefetches are always issued, from past the rows'
-        // end when there is no next chunk, in the order of the first loads,
-        // so that each wait of the load counter is exact)
-        const int tn = tnext >= 0 ? tnext : kNoRow;
         store_vt<TPR, kTRow>(sVT, cg, r, R.v);
         load_one<TPR>(R.v, rs.v, tn, r, cg);
         gates_scan_gt<16 * TPR>(R.g, R.th, t0, T, r, l, l2a, l2b, lend);
@@ -619,7 +622,7 @@ __device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1>
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) rho[e] += lend[e];
-    if (!LR || tnext >= 0) load_one<TPR>(R.k, rs.k, tnext >= 0 ? tnext : kNoRow, r, cg);
+    load_one<TPR>(R.k, rs.k, tn, r, cg);
 #pragma unroll
     for (int e = 0; e < 8; ++e) store_t_rows<TPR, kTRow>(sKbT, 8 * cg + e, r, kbT[e]);
     __syncthreads();
@@ -683,24 +686,17 @@ void scan_state_kernel(Params p) {
     Raw<CS, false, LR> Ra, Rb;
     Zops<1> Za, Zb;
     const int c0 = nch - 1;
-    if constexpr (LR) {
-        if (c0 >= 0) {
-            load_raw<CS, false>(Ra, rs, t_begin + c0 * CS, r, cg);
-            load_zops<1>(Za, rzg, rzt, t_begin + c0 * CS, l);
-        }
-        if (c0 >= 1) {
-            load_raw<CS, false>(Rb, rs, t_begin + (c0 - 1) * CS, r, cg);
-            load_zops<1>(Zb, rzg, rzt, t_begin + (c0 - 1) * CS, l);
-        }
-    } else {
+    {
         // the first two chunks in the order of the loop's prefetches (v, then
-        // g and th, then k), always issued
+        // the gate inputs, then k), always issued
         const int ta = c0 >= 0 ? t_begin + c0 * CS : kNoRow, tb = c0 >= 1 ? t_begin + (c0 - 1) * CS : kNoRow;
         load_one<TPR>(Ra.v, rs.v, ta, r, cg);
-        load_gates<CS, false>(Ra, rs, ta, r, cg);
+        if constexpr (LR) load_zops<1>(Za, rzg, rzt, ta, l);
+        else load_gates<CS, false>(Ra, rs, ta, r, cg);
         load_one<TPR>(Ra.k, rs.k, ta, r, cg);
         load_one<TPR>(Rb.v, rs.v, tb, r, cg);
-        load_gates<CS, false>(Rb, rs, tb, r, cg);
+        if constexpr (LR) load_zops<1>(Zb, rzg, rzt, tb, l);
+        else load_gates<CS, false>(Rb, rs, tb, r, cg);
         load_one<TPR>(Rb.k, rs.k, tb, r, cg);
     }
     for (int c = c0; c >= 0; c -= 2) {
