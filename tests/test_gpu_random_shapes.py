@@ -67,6 +67,33 @@ def test_prefill_random_shape(c):
     assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
 
 
+def _lowrank_cases(n, seed, tmax):
+    rng = np.random.default_rng(seed)
+    return [dict(seed=seed * 100 + i, B=int(rng.integers(1, 4)), H=int(rng.integers(1, 20)),
+                 T=int(rng.integers(1, tmax)), chunk=int(rng.choice([32, 64])), S0=bool(rng.random() < 0.5))
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("c", _lowrank_cases(20, 77, 1500),
+                         ids=lambda c: f"B{c['B']}H{c['H']}T{c['T']}-C{c['chunk']}-S0{int(c['S0'])}")
+def test_prefill_lowrank_random_shape(c):
+    """The low-rank prefill (bf16, d = 128, rank-16 gate factors) on random
+    batch, head and length counts, which vary the segment plan: one segment,
+    several with their states folded by the output pass, or many through the
+    combine pass, and ragged last chunks."""
+    names = ("q", "k", "v", "zg", "zt", "Ug", "bg", "Ut", "bt")
+    log(f"prefill_lowrank B{c['B']} H{c['H']} T{c['T']} C{c['chunk']} S0={c['S0']}")
+    x = workloads.lowrank_inputs(c["seed"], c["B"], c["H"], c["T"], 128, 128)
+    S0 = _state(np.random.default_rng(c["seed"] + 1), dict(c, dk=128, dv=128), c["S0"])
+    d = {n: dev(x[n]) for n in names}
+    o, ST = rd.rodimus_scan_prefill_lowrank(*(d[n] for n in names), S0=_cuda(S0), chunk=c["chunk"])
+    torch.cuda.synchronize()
+    ro, rST = oracle.scan_lowrank(*(x[n].f64() for n in names), S0=_f64(S0), nthreads=8)
+    eo, es = err(host(o), ro), err(host(ST), rST)
+    log(f"  err o {eo:.2e} S_T {es:.2e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("c", _scan_cases(24, 72, 400),
                          ids=lambda c: f"{c['dtype']}-B{c['B']}H{c['H']}T{c['T']}-{c['dk']}x{c['dv']}-mu{c['gate_mu']}")
 def test_backward_random_shape(c):
