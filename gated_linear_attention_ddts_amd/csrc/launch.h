@@ -70,8 +70,9 @@ struct SkaDecArgs {
 };
 
 // Longest-first order of the sequences of a packed batch (seq_order.hip):
-// order[rank] = sequence, for N <= kOrderMax (else none: table order).  It sits
-// in the workspace after the plan's own bytes (seq_order_bytes(N) of them).
+// order[rank] = sequence, ranked by length for N <= kOrderMax and counted by
+// 64-token chunk count above that.  It sits in the workspace after the plan's
+// own bytes (seq_order_bytes(N) of them).
 constexpr int kOrderMax = 4096;
 size_t seq_order_bytes(int N);
 void launch_seq_order(const int *cu, int N, int total, int T, int *order, hipStream_t st);

@@ -208,9 +208,10 @@ int rodimus_scan_prefill_noalloc(const void *q, const void *k, const void *v, co
  *   max_seqlen   : at least the longest sequence; it sizes the segment plan
  *                  and the workspace (query with the _workspace_bytes call)
  *
- * The workspace also holds, for N <= 4096, the order in which the sequences
- * are processed (longest first, computed on the device from the table), so
- * that long requests do not start last; it never changes the results.
+ * The workspace also holds the order in which the sequences are processed
+ * (longest first, computed on the device from the table: ranked by length up
+ * to 4096 sequences, by 64-token chunk count beyond), so that long requests
+ * do not start last; it never changes the results.
  *
  * Each sequence gives exactly what rodimus_scan_prefill gives for it alone
  * (same arithmetic; bitwise equal to a batched call of equal-length
@@ -283,7 +284,7 @@ int rodimus_scan_backward(const void *q, const void *k, const void *v, const voi
  *                  selects the path exactly as T does for rodimus_scan_backward
  *
  * As for the packed prefill, the workspace also holds the longest-first order
- * of the sequences (N <= 4096), which never changes the results.
+ * of the sequences, which never changes the results.
  *
  * Each sequence gets exactly the gradients that rodimus_scan_backward gives
  * for it alone (bitwise equal to a batched call of equal-length sequences).

@@ -135,7 +135,7 @@ def test_varlen_malformed_offsets_stay_in_bounds():
 
 @pytest.mark.parametrize("N", [4096, 5000])
 def test_varlen_many_short_sequences(N):
-    # N = 4096: the largest batch processed longest first; N = 5000: table order
+    # N = 4096: the largest batch ranked by length; N = 5000: ordered by chunk count
     rng = np.random.default_rng(350 + N)
     lengths = rng.integers(0, 10, size=N)
     lengths[N // 2] = 200                       # one long request in the middle
@@ -150,3 +150,35 @@ def test_varlen_many_short_sequences(N):
         eo = err(o[None, :, a:b], ro) if b > a else 0.0
         assert eo <= TOL["bf16"] and es <= TOL["bf16"], (N, s, b - a, eo, es)
     log(f"  {N} sequences: {len(picks)} checked")
+
+
+@pytest.mark.parametrize("N", [3000, 5000, 20000])
+def test_varlen_order_in_workspace(N):
+    """The longest-first order the packed prefill writes into its workspace
+    after the plan's own bytes: ranked by length, ties by index, up to 4096
+    sequences; counted by 64-token chunk count beyond (equal counts in any
+    order).  Either way a permutation of the sequences."""
+    rng = np.random.default_rng(360 + N)
+    lengths = rng.integers(0, 300, size=N)
+    lengths[N // 3] = 2000                      # one long request
+    lengths[rng.integers(0, N, size=20)] = 0    # and some empty ones
+    H, d = 1, 128
+    x, cu, _ = _packed(361, H, lengths, d, d, "bf16", with_state=False)
+    maxlen = int(lengths.max())
+    base = rd.rodimus_scan_prefill_workspace_bytes(N, H, maxlen, d, d, 64, rd.BF16)
+    need = rd.rodimus_scan_prefill_varlen_workspace_bytes(N, H, maxlen, d, d, 64, rd.BF16)
+    assert need - base >= 4 * N
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dd = {n: dev(x[n]) for n in NAMES}
+    rd.rodimus_scan_prefill_varlen(dd["q"], dd["k"], dd["v"], dd["g"], dd["theta"], torch.from_numpy(cu).cuda(),
+                                   maxlen, None, 64, workspace=ws, want_state=False)
+    torch.cuda.synchronize()
+    order = ws[base:base + 4 * N].view(torch.int32).cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(N))
+    if N <= 4096:
+        assert np.array_equal(order, np.lexsort((np.arange(N), -lengths)))
+    else:
+        key = np.minimum((lengths + 63) // 64, 4095)[order]
+        assert np.all(key[:-1] >= key[1:])
+    log(f"  {N} sequences: order checked")
+

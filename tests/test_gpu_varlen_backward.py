@@ -178,7 +178,7 @@ def test_varlen_backward_malformed_offsets_stay_in_bounds(dtype, d):
 
 @pytest.mark.parametrize("N", [4096, 5000])
 def test_varlen_backward_many_short_sequences(N):
-    # N = 4096: the largest batch processed longest first; N = 5000: table order
+    # N = 4096: the largest batch ranked by length; N = 5000: ordered by chunk count
     rng = np.random.default_rng(460 + N)
     lengths = rng.integers(0, 10, size=N)
     lengths[N // 3] = 150
