@@ -108,16 +108,31 @@ def test_scan_reset_gates():
 def test_scan_fast_decay_within_a_half(chunk):
     """g ~ N(-2, 0.5), theta ~ N(2, 0.5): about 2.7 log2 units of decay per token,
     so a 64-token chunk spans ~2^173 (beyond the factorised range) while each
-    32-token half spans ~2^86 (within it); a stretch of stronger decay (g ~ -4)
-    puts some halves beyond it too."""
+    32-token half spans ~2^86 (within it); a stretch of much stronger decay
+    (g ~ -8, about 10 log2 units per token) puts some halves beyond it, into
+    the token-by-token branch."""
     B, H, T, dk, dv = 1, 3, 900, 128, 128
     x = workloads.scan_inputs(17, B, H, T, dk, dv, "bf16")
     rng = np.random.default_rng(9)
     g = -2 + 0.5 * rng.standard_normal(x["g"].shape)
-    g[:, :, 500:560] -= 2.0
+    g[:, :, 500:560] -= 6.0
     x["g"] = workloads.Tensor(workloads.round_to(g, "bf16"), "bf16")
     x["theta"] = workloads.Tensor(workloads.round_to(2 + 0.5 * rng.standard_normal(x["g"].shape), "bf16"), "bf16")
     log(f"scan fast decay C={chunk}")
+    check(x, chunk, "bf16")
+
+
+@pytest.mark.parametrize("chunk", [64, 32])
+def test_scan_decay_just_past_the_factorised_range(chunk):
+    """g ~ N(-3, 0.5), theta ~ N(3, 0.5): about 4.2 log2 units of decay per
+    token, ~2^134 per 32-token half, just past the factorised range (Kh would
+    reach 2^134): every chunk takes the token-by-token branch."""
+    B, H, T, dk, dv = 1, 2, 700, 128, 128
+    x = workloads.scan_inputs(18, B, H, T, dk, dv, "bf16")
+    rng = np.random.default_rng(10)
+    x["g"] = workloads.Tensor(workloads.round_to(-3 + 0.5 * rng.standard_normal(x["g"].shape), "bf16"), "bf16")
+    x["theta"] = workloads.Tensor(workloads.round_to(3 + 0.5 * rng.standard_normal(x["g"].shape), "bf16"), "bf16")
+    log(f"scan decay just past the factorised range C={chunk}")
     check(x, chunk, "bf16")
 
 
