@@ -91,8 +91,11 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_o
 
 // ------------------------------------------------------------------ producer
 // Producer lane (256 of them): channel group cg (channels 8cg..8cg+7) and
-// token group r (tokens TPR*r .. TPR*r+TPR-1); the 16 lanes of a DPP row
-// share cg and together cover the C tokens of the chunk.
+// token group r (tokens TPR*r .. TPR*r+TPR-1).  In the 16-row layout the 16
+// lanes of a DPP row share cg and together cover the C tokens of the chunk;
+// in the by-halves layout (chunk_scan_half) lanes 8 apart take consecutive
+// token groups of one half and the 8 lanes of a block one 128-byte piece of a
+// row.  The loaders below take any (r, cg).
 // LR: the gate inputs come separately (Zops); g and th are then unused.
 template <int C, bool WITH_Q, bool LR = false>
 struct Raw {
