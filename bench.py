@@ -69,7 +69,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 NAMES = ("q", "k", "v", "g", "theta")
 CSRC = os.path.join(ROOT, "gated_linear_attention_ddts_amd", "csrc")
 KERNEL_SOURCES = {
-    "prefill": ("scan_mfma.hip", "mfma_common.h", "device_common.h"),
+    "prefill": ("scan_mfma.hip", "scan_state.hip", "scan_mfma.h", "mfma_common.h", "device_common.h"),
     "decode": ("decode.hip", "device_common.h"),
     "swska": ("swska.hip", "device_common.h"),
     "swska_decode": ("swska_decode.hip", "device_common.h"),
@@ -103,11 +103,15 @@ def _code_only(text: str) -> str:
 
 
 def source_hash(kind: str) -> str:
-    """Hash of the code (comments and whitespace removed) of a kernel's sources."""
+    """Hash of the code (comments and whitespace removed) of a kernel's sources
+    and of their per-file compiler options."""
+    from gated_linear_attention_ddts_amd.build import FILE_FLAGS
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
+        if f in FILE_FLAGS:   # compiler options change the code too
+            h.update(" ".join(FILE_FLAGS[f]).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,6 +35,13 @@ FLAGS = [
 # mode off, which drops the NaN-canonicalising moves in front of every min/max.
 FILE_FLAGS = {
     "scan_mfma.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    # The prefill's state pass and the backward's kernels are scheduled for
+    # instruction-level parallelism (measured: state pass 51.9 -> 50.7 us,
+    # backward gradient kernel 360.2 -> 354.7 us per call, bit-identical
+    # results); the output pass and SW-SKA keep the default scheduler, under
+    # which they are faster.
+    "scan_state.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "scan_bwd_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

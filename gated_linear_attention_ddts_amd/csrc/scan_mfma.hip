@@ -25,7 +25,7 @@
 // Segment-parallel form.  So that the grid fills the GPU when B*H is small, the
 // sequence of each (b, h) is cut into G segments (each a whole number of
 // chunks), and every segment but the last into P sub-segments:
-//   phase 1 (scan_state_kernel): each sub-segment's local end state (from zero)
+//   phase 1 (scan_state_kernel, scan_state.hip): each sub-segment's local end state (from zero)
 //            and its total log2 decay, in 32-token chunks with two chunks of
 //            inputs in flight.  Chunks are visited last to first, so the
 //            decay of the later chunks folds into the operand exponent:
@@ -64,23 +64,19 @@
 #include <algorithm>
 
 #include "launch.h"
-#include "mfma_common.h"
+#include "scan_mfma.h"
 
 namespace rodimus {
 
 namespace {
 
+using namespace prefill;
+
 constexpr int kCUs = 256;
 constexpr int kFoldMax = 8;        // sub-segment states a consumer wave folds itself
-constexpr int kMaxT = 1 << 23;     // 32-bit buffer offsets (T * 256 bytes)
-// A chunk start whose rows lie past the end of every descriptor (T < kMaxT):
-// loads from it return zeros and fetch nothing, and its byte offsets, up to
-// (kMaxT + 63) * 256 + 240, still fit 32 bits.
-constexpr int kNoRow = kMaxT;
 
 // LDS buffer layout (bytes); rows padded by 16 bytes (conflict-free 16-byte reads)
 constexpr int kQRow = kD + 8;      // bf16 per row of sQ / sK       [C][128]
-constexpr int kTRow = 64 + 8;      // bf16 per row of sKbT / sVT    [128][C]
 constexpr int kOffQ = 0;
 constexpr int kOffK = kOffQ + 64 * kQRow * 2;
 constexpr int kOffKbT = kOffK + 64 * kQRow * 2;
@@ -89,45 +85,6 @@ constexpr int kOffGam = kOffVT + kD * kTRow * 2;   // 2^{decay} of each half: [2
 constexpr int kBufBytes = kOffGam + 2 * kD * 4;
 constexpr int kARow = 64 + 8;      // bf16 per row of sA [C][C] (token i, token j permuted)
 constexpr int kSABytes = 64 * kARow * 2;
-
-struct Params {
-    const bf16_t *q, *k, *v, *g, *th;
-    const float *S0;  // [BH][128][128] or null (zeros)
-    bf16_t *o;
-    float *S_T;       // [BH][128][128] or null
-    float *wsS;       // [(G-1)*P][BH][16][256] float4: sub-segment states (lane-major) / incoming states
-    float *wsA;       // [(G-1)*P][BH][128] total decay of each sub-segment (a power of two)
-    int BH, T, G, seg_len, P, sub_len;
-    int fold;         // the output pass folds the sub-segment states itself (no combine)
-    // packed variable-length batch: sequence s = bh / H occupies rows
-    // cu[s] .. cu[s+1]-1 of head h = bh % H's [total][128] rows; T is then the
-    // longest length (the segment plan)
-    const int *cu;
-    int H, total;
-    const int *order;  // packed batch: longest-first order of the sequences, or null
-    // low-rank gates (LR kernels): factor rows zg, zt [B][T][16] bf16 shared by
-    // the heads; per-head factors Ug, Ut [H][128][16] bf16 and biases bg, bt
-    // [H][128] fp32
-    const bf16_t *zg, *zt, *Ug, *Ut;
-    const float *bg, *bt;
-};
-
-// Rows of (b,h): first row and length.  The packed form clamps each span to
-// [0, total] and to T, so a malformed offset table cannot address memory
-// outside the inputs and outputs.
-template <bool VL>
-__device__ __forceinline__ void seq_span(const Params &p, int bh, size_t &rowbase, int &len) {
-    if (!VL) {
-        rowbase = (size_t)bh * p.T;
-        len = p.T;
-        return;
-    }
-    const int s = bh / p.H, h = bh - s * p.H;
-    const int a = min(max(uni(p.cu[s]), 0), p.total);
-    const int b = min(max(uni(p.cu[s + 1]), a), p.total);
-    rowbase = (size_t)h * p.total + a;
-    len = min(b - a, p.T);
-}
 
 // The four consumer waves meet (an LDS counter; the producer waves are not
 // involved), with a bounded wait.  Returns true if the wait gave up: what the
@@ -579,147 +536,6 @@ void scan_full_kernel(Params p) {
     }
 }
 
-// ----------------------------------------------------------- phase 1 (state)
-// One sub-segment's local end state.  Processed in chunks of 32 tokens whatever
-// the caller's C (the result does not depend on the chunking), which leaves
-// room in the registers for two chunks of raw inputs in flight.
-template <int TPR, bool LR>
-__device__ __forceinline__ void state_chunk(Raw<16 * TPR, false, LR> &R, Zops<1> &Z, const LrOps &ops,
-                                            __amdgpu_buffer_rsrc_t rzg, __amdgpu_buffer_rsrc_t rzt, const Rsrc &rs,
-                                            int t0, int tnext, char *sKbT, char *sVT, f32x16_t (&S)[4],
-                                            float (&rho)[8], int r, int cg, int l, int w, int h, int l32, int T) {
-    float l2a[TPR][8], l2b[TPR][8], lend[8];
-    // The prefetches are always issued, from past the rows' end when there is
-    // no next chunk, in the order of the first loads (v, then the gate inputs,
-    // then k), so that each wait of the in-order load counter is exact.
-    const int tn = tnext >= 0 ? tnext : kNoRow;
-    if constexpr (LR) {
-        // logits of the 32-token chunk on the matrix cores, staged in this
-        // wave's rows of the K-bar^T (g) and V^T (tau) areas
-        lr_stage<1, kTRow>(Z, ops, sKbT, sVT, w, l);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        uint32_t gw[8][TPR / 2], tw[8][TPR / 2];
-        lr_read<TPR, kTRow>(sKbT, sVT, r, cg, gw, tw);
-        store_vt<TPR, kTRow>(sVT, cg, r, R.v);   // after the reads, in LDS order
-        load_one<TPR>(R.v, rs.v, tn, r, cg);
-        load_zops<1>(Z, rzg, rzt, tn, l);
-        gates_scan_cols<16 * TPR>(gw, tw, t0, T, r, l, l2a, l2b, lend);
-    } else {
-        store_vt<TPR, kTRow>(sVT, cg, r, R.v);
-        load_one<TPR>(R.v, rs.v, tn, r, cg);
-        gates_scan_gt<16 * TPR>(R.g, R.th, t0, T, r, l, l2a, l2b, lend);
-        load_gates<16 * TPR, false>(R, rs, tn, r, cg);
-    }
-    float kbT[8][TPR];
-#pragma unroll
-    for (int tt = 0; tt < TPR; ++tt) {
-        float kf[8];
-        unpack8(R.k[tt], kf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            kbT[e][tt] = kf[e] * exp2_fast(l2b[tt][e] + lend[e] - l2a[tt][e] + rho[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rho[e] += lend[e];
-    load_one<TPR>(R.k, rs.k, tn, r, cg);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) store_t_rows<TPR, kTRow>(sKbT, 8 * cg + e, r, kbT[e]);
-    __syncthreads();
-    bf16x8_t vB[TPR];
-#pragma unroll
-    for (int s = 0; s < TPR; ++s) vB[s] = lds16(sVT, ((32 * w + l32) * kTRow + 16 * s + 8 * h) * 2);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int s = 0; s < TPR; ++s)
-            S[mt] = mfma(lds16(sKbT, ((32 * mt + l32) * kTRow + 16 * s + 8 * h) * 2), vB[s], S[mt]);
-    __syncthreads();
-}
-
-template <bool VL, bool LR>
-__global__ __launch_bounds__(256, 2)
-void scan_state_kernel(Params p) {
-    constexpr int CS = 32, TPR = CS / 16;
-    __shared__ __attribute__((aligned(16))) char smem[2 * kD * kTRow * 2];
-    char *sKbT = smem, *sVT = smem + kD * kTRow * 2;
-
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, l32 = l & 31;
-    const int nsub = (p.G - 1) * p.P;
-    const int sub = uni(blockIdx.x / p.BH);
-    if (sub >= nsub) return;
-    const int bh = VL ? seq_head(p.order, p.H, uni(blockIdx.x % p.BH)) : uni(blockIdx.x % p.BH);
-    const int seg = sub / p.P, part = sub % p.P;
-    const int seg_begin = seg * p.seg_len;
-    const int t_begin = seg_begin + part * p.sub_len;
-    const int t_end = min(seg_begin + p.seg_len, t_begin + p.sub_len);  // whole chunks
-    size_t rowbase;
-    int Tb;
-    seq_span<VL>(p, bh, rowbase, Tb);
-    // chunks of this sub-segment that hold tokens (all of them unless packed)
-    const int nch = VL ? max(0, min((t_end - t_begin) / CS, (Tb - t_begin + CS - 1) / CS)) : (t_end - t_begin) / CS;
-    const int r = l & 15, cg = (w << 2) | (l >> 4);
-
-    Rsrc rs;
-    rs.k = rsrc(p.k + rowbase * kD, Tb); rs.v = rsrc(p.v + rowbase * kD, Tb);
-    __amdgpu_buffer_rsrc_t rzg, rzt;
-    LrOps ops;
-    if constexpr (LR) {
-        const size_t zrow = (size_t)(bh / p.H) * p.T;
-        rzg = rsrc_bytes(p.zg + zrow * kRank, Tb * (int)kZRow);
-        rzt = rsrc_bytes(p.zt + zrow * kRank, Tb * (int)kZRow);
-        lr_load_ops(ops, p.Ug, p.bg, p.Ut, p.bt, bh % p.H, w, l);
-    } else {
-        rs.g = rsrc(p.g + rowbase * kD, Tb);
-        rs.th = rsrc(p.th + rowbase * kD, Tb);
-    }
-    rs.q = rs.k;
-
-    f32x16_t S[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) S[mt] = f32x16_t{};
-    float rho[8];  // log2 decay of the chunks after the current one, per channel
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rho[e] = 0.f;
-
-    // chunks are visited last to first; two chunks of raw inputs are in flight
-    Raw<CS, false, LR> Ra, Rb;
-    Zops<1> Za, Zb;
-    const int c0 = nch - 1;
-    {
-        // the first two chunks in the order of the loop's prefetches (v, then
-        // the gate inputs, then k), always issued
-        const int ta = c0 >= 0 ? t_begin + c0 * CS : kNoRow, tb = c0 >= 1 ? t_begin + (c0 - 1) * CS : kNoRow;
-        load_one<TPR>(Ra.v, rs.v, ta, r, cg);
-        if constexpr (LR) load_zops<1>(Za, rzg, rzt, ta, l);
-        else load_gates<CS, false>(Ra, rs, ta, r, cg);
-        load_one<TPR>(Ra.k, rs.k, ta, r, cg);
-        load_one<TPR>(Rb.v, rs.v, tb, r, cg);
-        if constexpr (LR) load_zops<1>(Zb, rzg, rzt, tb, l);
-        else load_gates<CS, false>(Rb, rs, tb, r, cg);
-        load_one<TPR>(Rb.k, rs.k, tb, r, cg);
-    }
-    for (int c = c0; c >= 0; c -= 2) {
-        state_chunk<TPR, LR>(Ra, Za, ops, rzg, rzt, rs, t_begin + c * CS, c >= 2 ? t_begin + (c - 2) * CS : -1,
-                             sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
-        if (c >= 1)
-            state_chunk<TPR, LR>(Rb, Zb, ops, rzg, rzt, rs, t_begin + (c - 1) * CS,
-                                 c >= 3 ? t_begin + (c - 3) * CS : -1, sKbT, sVT, S, rho, r, cg, l, w, h, l32, Tb);
-    }
-    float4 *So = reinterpret_cast<float4 *>(p.wsS + ((size_t)sub * p.BH + bh) * kD * kD) + 64 * w + l;
-#pragma unroll
-    for (int k4 = 0; k4 < 16; ++k4) {
-        const f32x16_t &A = S[k4 >> 2];
-        const int i = 4 * (k4 & 3);
-        So[256 * k4] = make_float4(A[i + 0], A[i + 1], A[i + 2], A[i + 3]);
-    }
-    if (r == 0) {
-        float *A = p.wsA + ((size_t)sub * p.BH + bh) * kD + 8 * cg;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) A[e] = exp2_fast(rho[e]);
-    }
-}
-
 // Phase 2 when the output pass does not fold: run the sub-segment states left
 // to right, S <- diag(2^{A_j}) S + S_loc[j], storing S into the slot of the
 // last sub-segment of every segment (the incoming state of the next segment).
@@ -837,10 +653,7 @@ void launch_scan_mfma(const ScanArgs &a, const ScanPlan &pl, hipStream_t st) {
     p.Ug = (const bf16_t *)a.Ug; p.Ut = (const bf16_t *)a.Ut; p.bg = a.bg; p.bt = a.bt;
     const bool vl = a.cu != nullptr, lr = a.zg != nullptr;
     if (q.G > 1) {
-        const dim3 g1(nsub * BH), b1(256);
-        if (lr) hipLaunchKernelGGL((scan_state_kernel<false, true>), g1, b1, 0, st, p);
-        else if (vl) hipLaunchKernelGGL((scan_state_kernel<true, false>), g1, b1, 0, st, p);
-        else hipLaunchKernelGGL((scan_state_kernel<false, false>), g1, b1, 0, st, p);
+        launch_scan_state(p, vl, lr, (unsigned)(nsub * BH), st);
         if (!p.fold) {
             const size_t n4 = (size_t)BH * kD * kD / 4;
             hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
