@@ -46,3 +46,22 @@ def test_swska_decode_bytes_per_sequence_step():
     # key window + one head's value window, q, k_new, v_new in; k_new, v_new to the caches; o out
     w, d = 4096, 128
     assert bench.swska_decode_bytes(1, 1, d, d, w) == 2 * w * d * 2 + d * 2 + 2 * (2 * d * 2) + d * 2
+
+
+def test_source_hash_covers_every_source_and_its_compiler_options(monkeypatch):
+    # the traffic records are tied to the code the counters were taken on: every
+    # source of a kernel (the prefill's state pass is a unit of its own) and the
+    # per-file compiler options count
+    import gated_linear_attention_ddts_amd.build as build
+    csrc = os.path.join(ROOT, "gated_linear_attention_ddts_amd", "csrc")
+    for kind, files in bench.KERNEL_SOURCES.items():
+        assert all(os.path.exists(os.path.join(csrc, f)) for f in files), kind
+    assert {"scan_mfma.hip", "scan_state.hip", "scan_mfma.h"} <= set(bench.KERNEL_SOURCES["prefill"])
+    before, other = bench.source_hash("prefill"), bench.source_hash("decode")
+    flags = dict(build.FILE_FLAGS)
+    flags["scan_state.hip"] = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
+    monkeypatch.setattr(build, "FILE_FLAGS", flags)
+    assert bench.source_hash("prefill") != before
+    assert bench.source_hash("decode") == other
+    monkeypatch.undo()
+    assert bench.source_hash("prefill") == before
